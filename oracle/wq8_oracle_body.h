@@ -1,0 +1,229 @@
+/*
+ * Fixed-order quantized Winograd pipeline, written once and compiled twice by
+ * wq8_oracle.c: with REAL = float (the parity target, "O-C") and with
+ * REAL = double (used by the brute-force Kronecker pin, where summation order
+ * cannot flip a code).
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may include, link or
+ * call this file; only tests/, the smoke check and the benchmark's CPU
+ * baseline do.
+ *
+ * Method: "Data-Free Group-Wise Fully Quantized Winograd Convolution via
+ * Learnable Scales" (arXiv 2412.19867). The pages describe group-wise
+ * quantization at every stage of the Winograd pipeline (input transform,
+ * Hadamard product, output transform; referee summary and the "Approach"
+ * section of the AI summary page, Fig. 2 caption) and name the quantized
+ * Winograd-domain output Y (Eq. 5) whose cross-shaped range a single scale
+ * per tile cannot hold (core claim, Fig. 3 caption).
+ *
+ * Readings taken where the pages are silent (each also listed in the design doc):
+ *  - quantization points are V (input transform), U (weight transform) and
+ *    Y (Hadamard output); transform matrices stay fp32, x is not quantized
+ *    before the transform;
+ *  - V and U groups are G consecutive input channels inside one tap; Y has
+ *    one scale per (tile, output channel) spanning all n*n taps;
+ *  - symmetric absmax quantizer, codes in [-127, 127], scale = absmax/127,
+ *    code = rint(x * (127/absmax)) with ties to even; an all-zero group gives
+ *    codes 0 and scale 0;
+ *  - every fp32 sum is a left-to-right fma chain starting from +0.
+ *
+ * Expects the includer to define REAL, SUF(name), FMA, RINT, FABS.
+ */
+
+/* Symmetric absmax quantizer over len values spaced `stride` apart. */
+static void SUF(quantize)(const REAL *v, long stride, int len, int8_t *q,
+                          long qstride, REAL *scale)
+{
+    REAL a = 0;
+    for (int i = 0; i < len; ++i) {
+        REAL mag = FABS(v[i * stride]);
+        if (mag > a)
+            a = mag;
+    }
+    if (a == 0) {
+        for (int i = 0; i < len; ++i)
+            q[i * qstride] = 0;
+        *scale = 0;
+        return;
+    }
+    REAL inv = (REAL)127 / a;
+    for (int i = 0; i < len; ++i) {
+        REAL r = RINT(v[i * stride] * inv);
+        if (r > 127)
+            r = 127;
+        if (r < -127)
+            r = -127;
+        q[i * qstride] = (int8_t)r;
+    }
+    *scale = a / (REAL)127;
+}
+
+/*
+ * Weight transform U = G g G^T for every (co, ci), then per-group
+ * quantization along ci.
+ *   w  : [Cout][Cin][3][3]
+ *   Gm : [n][3] (already carrying S_G)
+ *   Uq : [n*n][Cout][Cin] int8,  sU : [n*n][Cout][Cin/G]
+ */
+void SUF(wq8o_weights)(int m, int Cin, int Cout, int G, const REAL *Gm,
+                       const float *w, int8_t *Uq, REAL *sU)
+{
+    const int n = m + 2, n2 = n * n, ng = Cin / G;
+#pragma omp parallel for schedule(static)
+    for (int co = 0; co < Cout; ++co) {
+        REAL *U = (REAL *)malloc(sizeof(REAL) * (size_t)n2 * Cin); /* [tap][ci] */
+        for (int ci = 0; ci < Cin; ++ci) {
+            const float *g = w + ((size_t)co * Cin + ci) * 9;
+            REAL t2[16][3];
+            for (int i = 0; i < n; ++i)
+                for (int b = 0; b < 3; ++b) {
+                    REAL acc = 0;
+                    for (int a = 0; a < 3; ++a)
+                        acc = FMA(Gm[i * 3 + a], (REAL)g[a * 3 + b], acc);
+                    t2[i][b] = acc;
+                }
+            for (int i = 0; i < n; ++i)
+                for (int j = 0; j < n; ++j) {
+                    REAL acc = 0;
+                    for (int b = 0; b < 3; ++b)
+                        acc = FMA(t2[i][b], Gm[j * 3 + b], acc);
+                    U[(size_t)(i * n + j) * Cin + ci] = acc;
+                }
+        }
+        for (int tap = 0; tap < n2; ++tap)
+            for (int gi = 0; gi < ng; ++gi)
+                SUF(quantize)(U + (size_t)tap * Cin + (size_t)gi * G, 1, G,
+                              Uq + ((size_t)tap * Cout + co) * Cin + (size_t)gi * G, 1,
+                              sU + ((size_t)tap * Cout + co) * ng + gi);
+        free(U);
+    }
+}
+
+/*
+ * Stage 1: input tiles d (n x n, zero outside the image), V = Bt d Bt^T, then
+ * per-group quantization along ci inside each (tap, tile).
+ *   x  : [N][Cin][H][W]
+ *   Bt : [n][n] (already carrying S_B)
+ *   Vq : [n*n][T][Cin] int8,  sV : [n*n][T][Cin/G]
+ * Tile t = (img*tH + ty)*tW + tx covers output rows ty*m .. ty*m+m-1 and
+ * reads input rows ty*m - pad .. ty*m - pad + n - 1 (columns likewise).
+ */
+void SUF(wq8o_stage1)(int m, int N, int Cin, int H, int W, int pad, int G,
+                      const REAL *Bt, const float *x, int8_t *Vq, REAL *sV)
+{
+    const int n = m + 2, n2 = n * n, ng = Cin / G;
+    const int Ho = H + 2 * pad - 2, Wo = W + 2 * pad - 2;
+    const int tH = (Ho + m - 1) / m, tW = (Wo + m - 1) / m;
+    const long T = (long)N * tH * tW;
+#pragma omp parallel for schedule(static)
+    for (long t = 0; t < T; ++t) {
+        const int img = (int)(t / ((long)tH * tW));
+        const int ty = (int)(t / tW % tH), tx = (int)(t % tW);
+        REAL *V = (REAL *)malloc(sizeof(REAL) * (size_t)n2 * Cin); /* [tap][ci] */
+        for (int ci = 0; ci < Cin; ++ci) {
+            REAL d[16][16], t1[16][16];
+            for (int k = 0; k < n; ++k)
+                for (int l = 0; l < n; ++l) {
+                    int h = ty * m - pad + k, ww = tx * m - pad + l;
+                    d[k][l] = (h >= 0 && h < H && ww >= 0 && ww < W)
+                                  ? (REAL)x[(((size_t)img * Cin + ci) * H + h) * W + ww]
+                                  : 0;
+                }
+            for (int i = 0; i < n; ++i)
+                for (int l = 0; l < n; ++l) {
+                    REAL acc = 0;
+                    for (int k = 0; k < n; ++k)
+                        acc = FMA(Bt[i * n + k], d[k][l], acc);
+                    t1[i][l] = acc;
+                }
+            for (int i = 0; i < n; ++i)
+                for (int j = 0; j < n; ++j) {
+                    REAL acc = 0;
+                    for (int l = 0; l < n; ++l)
+                        acc = FMA(t1[i][l], Bt[j * n + l], acc);
+                    V[(size_t)(i * n + j) * Cin + ci] = acc;
+                }
+        }
+        for (int tap = 0; tap < n2; ++tap)
+            for (int gi = 0; gi < ng; ++gi)
+                SUF(quantize)(V + (size_t)tap * Cin + (size_t)gi * G, 1, G,
+                              Vq + ((size_t)tap * T + t) * Cin + (size_t)gi * G, 1,
+                              sV + ((size_t)tap * T + t) * ng + gi);
+        free(V);
+    }
+}
+
+/*
+ * Stage 2: Hadamard product summed over input channels (Eq. 5), per tap:
+ *   P_g = sum_{ci in group g} Vq * Uq            (exact int32)
+ *   M   = fma(sV_g * sU_g, P_g, M) for g = 0, 1, ...  starting from +0
+ *   M  : [n*n][T][Cout]
+ */
+void SUF(wq8o_stage2)(int n2, long T, int Cin, int Cout, int G, const int8_t *Vq,
+                      const REAL *sV, const int8_t *Uq, const REAL *sU, REAL *M)
+{
+    const int ng = Cin / G;
+#pragma omp parallel for schedule(static) collapse(2)
+    for (int tap = 0; tap < n2; ++tap)
+        for (long t = 0; t < T; ++t)
+            for (int co = 0; co < Cout; ++co) {
+                const int8_t *v = Vq + ((size_t)tap * T + t) * Cin;
+                const int8_t *u = Uq + ((size_t)tap * Cout + co) * Cin;
+                REAL acc = 0;
+                for (int gi = 0; gi < ng; ++gi) {
+                    int32_t P = 0;
+                    for (int c = gi * G; c < (gi + 1) * G; ++c)
+                        P += (int32_t)v[c] * (int32_t)u[c];
+                    REAL s = sV[((size_t)tap * T + t) * ng + gi] *
+                             sU[((size_t)tap * Cout + co) * ng + gi];
+                    acc = FMA(s, (REAL)P, acc);
+                }
+                M[((size_t)tap * T + t) * Cout + co] = acc;
+            }
+}
+
+/*
+ * Stage 3: Y = M for one (tile, co) over all n*n taps, quantized with a single
+ * scale; output o = sY * (At Yq At^T), cropped to the image.
+ *   M  : [n*n][T][Cout],  At : [m][n] (already carrying S_A)
+ *   y  : [N][Cout][Ho][Wo]
+ *   Yq : [T][Cout][n*n] (optional),  sY : [T][Cout] (optional)
+ */
+void SUF(wq8o_stage3)(int m, int N, int Cout, int H, int W, int pad, const REAL *At,
+                      const REAL *M, REAL *y, int8_t *Yq_out, REAL *sY_out)
+{
+    const int n = m + 2, n2 = n * n;
+    const int Ho = H + 2 * pad - 2, Wo = W + 2 * pad - 2;
+    const int tH = (Ho + m - 1) / m, tW = (Wo + m - 1) / m;
+    const long T = (long)N * tH * tW;
+#pragma omp parallel for schedule(static) collapse(2)
+    for (long t = 0; t < T; ++t)
+        for (int co = 0; co < Cout; ++co) {
+            const int img = (int)(t / ((long)tH * tW));
+            const int ty = (int)(t / tW % tH), tx = (int)(t % tW);
+            int8_t yq[256];
+            REAL sy, z[16][16];
+            SUF(quantize)(M + (size_t)t * Cout + co, (long)T * Cout, n2, yq, 1, &sy);
+            for (int a = 0; a < m; ++a)
+                for (int j = 0; j < n; ++j) {
+                    REAL acc = 0;
+                    for (int i = 0; i < n; ++i)
+                        acc = FMA(At[a * n + i], (REAL)yq[i * n + j], acc);
+                    z[a][j] = acc;
+                }
+            for (int a = 0; a < m; ++a)
+                for (int b = 0; b < m; ++b) {
+                    REAL acc = 0;
+                    for (int j = 0; j < n; ++j)
+                        acc = FMA(z[a][j], At[b * n + j], acc);
+                    int h = ty * m + a, ww = tx * m + b;
+                    if (h < Ho && ww < Wo)
+                        y[(((size_t)img * Cout + co) * Ho + h) * Wo + ww] = acc * sy;
+                }
+            if (Yq_out)
+                for (int k = 0; k < n2; ++k)
+                    Yq_out[((size_t)t * Cout + co) * n2 + k] = yq[k];
+            if (sY_out)
+                sY_out[(size_t)t * Cout + co] = sy;
+        }
+}
