@@ -1,0 +1,162 @@
+"""Benchmark: quantized Winograd F(6,3) conv layer on one MI355X.
+
+Workload: the ResNet-18-shaped 3x3 layer (N=32, Cin=Cout=64, 56x56, pad 1,
+group 64, seeded exp(U(-1/2,1/2)) transform scales), synthetic seeded inputs.
+A step is one whole forward (input transform + int8 Hadamard GEMMs + output
+transform) with inputs and prepared weights resident in HBM; the weight
+transform is done once before timing.
+
+Prints one JSON line: direct-conv-equivalent int8 TOPS, the per-kernel
+roofline of the dominant kernel (HIP events around each stage's kernel on the
+stream it runs on), and the CPU oracle timed on the host for comparison.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import quantized_convolution_amd as q  # noqa: E402
+from quantized_convolution_amd import workloads as WL  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POP/s)
+
+
+def stage_bytes(L, plan):
+    """Algorithmic HBM bytes of each kernel per launch (each operand read or
+    written once)."""
+    n2, T, ng = plan.n ** 2, plan.T, plan.ng
+    xb = L.N * L.Cin * L.H * L.W * 4
+    yb = L.N * L.Cout * L.Ho * L.Wo * 4
+    vq, sv = n2 * T * L.Cin, n2 * T * ng * 4
+    uq, su = n2 * L.Cout * L.Cin, n2 * L.Cout * ng * 4
+    mb = n2 * T * L.Cout * 4
+    return {"stage1": xb + vq + sv, "stage2": vq + sv + uq + su + mb, "stage3": mb + yb}
+
+
+def time_events(fn, iters, stream):
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters  # ms
+
+
+def cpu_baseline(L, d, min_seconds=10.0):
+    """The plain CPU oracle (as it stands) on the host cores, over the full
+    workload, repeated until about `min_seconds` of CPU work."""
+    import oracle
+    from oracle import transforms as T
+
+    Bt, Gm, At = T.transforms_f32(L.m, list(d["points"]), d["s_b"], d["s_g"])
+    Uq, sU = oracle.weights(L.m, d["w"], L.G, Gm)
+    times = []
+    t_end = time.perf_counter() + min_seconds
+    while len(times) < 3 or time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        Vq, sV = oracle.stage1(L.m, d["x"], L.pad, L.G, Bt)
+        M = oracle.stage2(Vq, sV, Uq, sU, L.G)
+        oracle.stage3(L.m, M, L.N, L.H, L.W, L.pad, At)
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 200:
+            break
+    t = statistics.median(times)
+    return {"value": round(L.direct_ops() / t / 1e12, 5), "unit": "TOPS",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"full workload (N={L.N}), forward only, median of {len(times)} runs, "
+                      f"{t * 1e3:.1f} ms each"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layer", default=WL.BENCH_LAYER, choices=sorted(WL.LAYERS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is not "
+              "sharded across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    L = WL.LAYERS[args.layer]
+    d = WL.make(L)
+    plan = q.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"],
+                  s_B=d["s_b"], s_G=d["s_g"])
+    x = torch.from_numpy(d["x"]).to(dev)
+    w = torch.from_numpy(d["w"]).to(dev)
+    Uq, sU = q.wq8_weights_prepare(plan, w)
+    y = plan.empty_output(dev)
+    ws = plan.empty_workspace(dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        q.wq8_conv_forward(plan, x, Uq, sU, y=y, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_events(step, args.steps, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tops = L.direct_ops() / (ms * 1e-3) / 1e12
+
+    # per-kernel durations: each stage entry point launches exactly the kernel
+    # the forward launches, with the same grid, on the same stream
+    n2 = plan.n ** 2
+    Vq = torch.empty((n2, plan.T, L.Cin), dtype=torch.int8, device=dev)
+    sV = torch.empty((n2, plan.T, plan.ng), dtype=torch.float32, device=dev)
+    M = torch.empty((n2, plan.T, L.Cout), dtype=torch.float32, device=dev)
+    iters = max(20, args.steps // 2)
+    k_ms = {
+        "stage1": time_events(lambda: q.wq8_stage1(plan, x, Vq, sV), iters, stream),
+        "stage2": time_events(lambda: q.wq8_stage2(plan, Vq, sV, Uq, sU, M), iters, stream),
+        "stage3": time_events(lambda: q.wq8_stage3(plan, M, y), iters, stream),
+    }
+    nbytes = stage_bytes(L, plan)
+    dom = max(k_ms, key=k_ms.get)
+    achieved = nbytes[dom] / (k_ms[dom] * 1e-3) / 1e9
+    stages = {k: {"us": round(v * 1e3, 2), "GB_s": round(nbytes[k] / (v * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(nbytes[k] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+              for k, v in k_ms.items()}
+    hop = 2 * n2 * plan.T * L.Cin * L.Cout
+    stages["stage2"]["int8_TOPS"] = round(hop / (k_ms["stage2"] * 1e-3) / 1e12, 2)
+    stages["stage2"]["mfma_frac"] = round(hop / (k_ms["stage2"] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 5)
+
+    out = {
+        "metric": "direct-conv-equiv int8 TOPS per layer, F(6,3); % MFMA int8 peak + HBM GB/s",
+        "value": round(tops, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": L.name, "m": L.m, "N": L.N, "Cin": L.Cin, "Cout": L.Cout,
+                   "H": L.H, "W": L.W, "pad": L.pad, "group": L.G, "scales": L.scales,
+                   "x_dtype": "f32", "tiles": plan.T},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": nbytes[dom]},
+        "stages": stages,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(L, d)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

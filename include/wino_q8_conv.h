@@ -1,0 +1,140 @@
+/*
+ * wino_q8_conv — group-wise fully quantized 8-bit Winograd convolution F(m,3)
+ * with diagonal transform scales, for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Data-Free Group-Wise Fully Quantized Winograd Convolution via
+ * Learnable Scales" (arXiv 2412.19867).
+ *   - Transforms from the Vandermonde factorization with diagonal scales,
+ *     B^T = S_B V^-T, G = S_G V, A^T = V^T S_A, S_A S_B S_G = I; only S_B and
+ *     S_G are free ("What carries the argument" on the review page). V is
+ *     built from homogeneous polynomial points, V[i][j] = f_i^j g_i^(b-1-j)
+ *     (appendix 7.1, "Standard Winograd transforms").
+ *   - Group-wise int8 quantization at every stage: input transform, Hadamard
+ *     product, output transform (referee summary; Fig. 2 caption).
+ *   - The Winograd-domain output Y (Eq. 5) is quantized with one scale that
+ *     spans all taps of a tile, the granularity whose cross-shaped range the
+ *     learned scales even out (core claim; Fig. 3 caption).
+ * The scales are inputs: learning them (the paper's Algorithm 1) is offline.
+ *
+ * Computation (n = m + 2, T tiles, tile t = (img*tH + ty)*tW + tx,
+ * tH = ceil(Ho/m), tW = ceil(Wo/m), Ho = H + 2 pad - 2, Wo likewise):
+ *   U  = G g G^T per (co, ci); codes/scales per group of G input channels
+ *        inside one tap:         Uq [n*n][Cout][Cin] int8, sU [n*n][Cout][Cin/G] f32
+ *   V  = B^T d B^T^T per (t, ci), d the n x n input patch (zero outside the
+ *        image):                  Vq [n*n][T][Cin] int8,   sV [n*n][T][Cin/G] f32
+ *   P_g = sum_{ci in g} Vq Uq (int32, exact)
+ *   M  = sum_g (sV_g sU_g) P_g as an fp32 fma chain over g: M [n*n][T][Cout] f32
+ *   Y  = M over the n*n taps of one (t, co), one scale: Yq [T][Cout][n*n], sY [T][Cout]
+ *   y  = sY * (A^T Yq A), cropped to Ho x Wo:  y [N][Cout][Ho][Wo]
+ * Quantizer: a = max|v| over the group; a == 0 -> codes 0, scale 0; otherwise
+ * code = clamp(rint(v * (127/a)), -127, 127) (ties to even), scale = a/127.
+ * All transform sums are fp32 fma chains in index order, so results are
+ * reproducible bit for bit.
+ *
+ * Convolution semantics: 3x3 cross-correlation, stride 1, zero padding `pad`
+ * (0..2), no bias, NCHW activations.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are caller-owned allocations on the current HIP device;
+ *     the library never allocates device memory and never synchronises.
+ *     All work is enqueued on `stream` (a hipStream_t; NULL = default stream)
+ *     and completes asynchronously; device faults surface at the caller's
+ *     next synchronisation.
+ *   - Device pointers must be 16-byte aligned. Arguments are checked before
+ *     anything is enqueued; on error nothing is launched and the status says
+ *     why (details in wq8_last_error()).
+ *   - Inputs must be finite; behaviour for NaN/Inf data is unspecified.
+ *   - A plan is immutable after creation and may be used from several host
+ *     threads on different streams, each with its own workspace.
+ */
+#ifndef WINO_Q8_CONV_H
+#define WINO_Q8_CONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WQ8_OK = 0,
+    WQ8_ERR_INVALID_ARG = -1,      /* a size, pointer or enum is out of range */
+    WQ8_ERR_UNSUPPORTED = -2,      /* valid, but not a configuration this build runs */
+    WQ8_ERR_SINGULAR_POINTS = -3,  /* points not distinct: V is singular */
+    WQ8_ERR_WORKSPACE_TOO_SMALL = -4,
+    WQ8_ERR_MISALIGNED = -5,       /* a device pointer is not 16-byte aligned */
+    WQ8_ERR_HIP = -6,              /* a HIP launch failed; see wq8_last_error() */
+    WQ8_ERR_NO_MEMORY = -7         /* host allocation for the plan failed */
+} wq8_status;
+
+typedef enum { WQ8_F32 = 0, WQ8_BF16 = 1 } wq8_dtype;
+
+typedef struct wq8_plan wq8_plan; /* opaque */
+
+typedef struct {
+    int m;                 /* output tile size: 4 or 6 (r = 3 fixed) */
+    const double *points;  /* n = m + 2 distinct points; +INFINITY is the point
+                              at infinity (homogeneous (1, 0)). NULL selects the
+                              standard points 0, 1, -1, 2, -2, [1/2, -1/2,] inf */
+    const float *s_B;      /* n diagonal entries of S_B, finite, non-zero; NULL = 1 */
+    const float *s_G;      /* n diagonal entries of S_G; S_A = (S_B S_G)^-1 */
+    int group;             /* G: 16, 32, 64, 128 or 256; Cin % G == 0 */
+    int N, Cin, Cout, H, W;
+    int pad;               /* 0, 1 or 2 */
+    wq8_dtype x_dtype;     /* activations in */
+    wq8_dtype y_dtype;     /* activations out */
+} wq8_desc;
+
+/* Validates the descriptor and builds the scaled transforms on the host (exact
+ * to long double, rounded once to fp32). No device work. The caller owns *out
+ * and frees it with wq8_plan_destroy. */
+wq8_status wq8_plan_create(const wq8_desc *desc, wq8_plan **out);
+void wq8_plan_destroy(wq8_plan *plan);
+
+/* Sizes in bytes of the forward workspace and of the prepared weights, and the
+ * tile count T. Any output pointer may be NULL. */
+wq8_status wq8_plan_query(const wq8_plan *plan, size_t *workspace_bytes,
+                          size_t *u_code_bytes, size_t *u_scale_bytes, int64_t *tiles);
+
+/* Host copies of the fp32 matrices the kernels use: Bt [n][n] (carries S_B),
+ * G [n][3] (carries S_G), At [m][n] (carries S_A). Any pointer may be NULL. */
+wq8_status wq8_plan_matrices(const wq8_plan *plan, float *Bt, float *G, float *At);
+
+/* Offline weight transform and quantization (U = G g G^T; per-group int8).
+ *   w  [Cout][Cin][3][3] f32 (device), Uq [n*n][Cout][Cin] int8 (device),
+ *   sU [n*n][Cout][Cin/G] f32 (device). */
+wq8_status wq8_weights_prepare(const wq8_plan *plan, const float *w, int8_t *Uq,
+                               float *sU, void *stream);
+
+/* The hot path: input transform + quantization, int8 Hadamard GEMMs with group
+ * dequantization, Y requantization + output transform + crop.
+ *   x [N][Cin][H][W] (x_dtype), y [N][Cout][Ho][Wo] (y_dtype), Uq/sU from
+ *   wq8_weights_prepare, workspace of at least the queried size (device,
+ *   256-byte aligned recommended). x and y must not overlap. */
+wq8_status wq8_conv_forward(const wq8_plan *plan, const void *x, const int8_t *Uq,
+                            const float *sU, void *y, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* Individual stages with the layouts above (for parity checks and profiling). */
+wq8_status wq8_stage1(const wq8_plan *plan, const void *x, int8_t *Vq, float *sV,
+                      void *stream);
+wq8_status wq8_stage2(const wq8_plan *plan, const int8_t *Vq, const float *sV,
+                      const int8_t *Uq, const float *sU, float *M, void *stream);
+/* int32 partial sums P [n*n][Cin/G][T][Cout], one per quantization group. */
+wq8_status wq8_stage2_i32(const wq8_plan *plan, const int8_t *Vq, const int8_t *Uq,
+                          int32_t *P, void *stream);
+/* Y requantization + output transform. Yq [T][Cout][n*n] and sY [T][Cout] are
+ * optional outputs (NULL to skip). */
+wq8_status wq8_stage3(const wq8_plan *plan, const float *M, void *y, int8_t *Yq,
+                      float *sY, void *stream);
+
+const char *wq8_status_string(wq8_status status);
+/* Detail of the last error on the calling host thread ("" if none). */
+const char *wq8_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WINO_Q8_CONV_H */

@@ -52,6 +52,8 @@ def lib():
             getattr(_lib, "wq8o_stage1" + s).argtypes = [i, i, i, i, i, i, i, P, P, P, P]
             getattr(_lib, "wq8o_stage2" + s).argtypes = [i, l, i, i, i, P, P, P, P, P]
             getattr(_lib, "wq8o_stage3" + s).argtypes = [i, i, i, i, i, i, P, P, P, P, P]
+            getattr(_lib, "wq8o_sampled" + s).argtypes = [i, l, i, i, i, P, P, P, P, P, i, P, P, P,
+                                                           P, P]
     return _lib
 
 
@@ -183,6 +185,26 @@ def stage3(m, M, N, H, W, pad, At, prec="f32"):
     getattr(lib(), "wq8o_stage3_" + prec)(m, N, Cout, H, W, pad, _p(At), _p(M), _p(y),
                                           _p(Yq), _p(sY))
     return y, Yq, sY
+
+
+def sampled(m, Vq, sV, Uq, sU, At, pairs, prec="f32"):
+    """Stages 2 and 3 at chosen (tile, co) pairs only: returns M [S][n*n],
+    Yq [S][n*n], sY [S] and the uncropped output tiles [S][m][m]."""
+    n2, T_, Cin = Vq.shape
+    Cout = Uq.shape[1]
+    G = Cin // sV.shape[2]
+    R = _real(prec)
+    pairs = np.ascontiguousarray(pairs, np.int64).reshape(-1, 2)
+    S = pairs.shape[0]
+    Ms = np.zeros((S, n2), R)
+    Yq = np.zeros((S, n2), np.int8)
+    sY = np.zeros(S, R)
+    ys = np.zeros((S, m, m), R)
+    sV, sU, At = (np.ascontiguousarray(a, R) for a in (sV, sU, At))
+    getattr(lib(), "wq8o_sampled_" + prec)(m, T_, Cin, Cout, G, _p(np.ascontiguousarray(Vq)), _p(sV),
+                                           _p(np.ascontiguousarray(Uq)), _p(sU), _p(At), S,
+                                           _p(pairs), _p(Ms), _p(Yq), _p(sY), _p(ys))
+    return Ms, Yq, sY, ys
 
 
 def forward(m, x, w, pad, G, points=None, s_b=None, s_g=None, prec="f32", keep=False):

@@ -227,3 +227,57 @@ void SUF(wq8o_stage3)(int m, int N, int Cout, int H, int W, int pad, const REAL 
                 sY_out[(size_t)t * Cout + co] = sy;
         }
 }
+
+/*
+ * Stages 2 and 3 evaluated only at chosen (tile, co) pairs, for checks at
+ * sizes where the full Hadamard stage is too slow on the CPU. Same
+ * definitions as wq8o_stage2 / wq8o_stage3, one pair at a time:
+ *   pairs : [S][2] (t, co)
+ *   Ms    : [S][n*n]   M over every tap of the pair
+ *   Yqs   : [S][n*n],  sYs : [S]
+ *   ys    : [S][m][m]  the output tile (uncropped)
+ */
+void SUF(wq8o_sampled)(int m, long T, int Cin, int Cout, int G, const int8_t *Vq,
+                       const REAL *sV, const int8_t *Uq, const REAL *sU, const REAL *At,
+                       int S, const long *pairs, REAL *Ms, int8_t *Yqs, REAL *sYs, REAL *ys)
+{
+    const int n = m + 2, n2 = n * n, ng = Cin / G;
+#pragma omp parallel for schedule(static)
+    for (int s = 0; s < S; ++s) {
+        const long t = pairs[2 * s];
+        const int co = (int)pairs[2 * s + 1];
+        REAL *Mv = Ms + (size_t)s * n2;
+        for (int tap = 0; tap < n2; ++tap) {
+            const int8_t *v = Vq + ((size_t)tap * T + t) * Cin;
+            const int8_t *u = Uq + ((size_t)tap * Cout + co) * Cin;
+            REAL acc = 0;
+            for (int gi = 0; gi < ng; ++gi) {
+                int32_t P = 0;
+                for (int c = gi * G; c < (gi + 1) * G; ++c)
+                    P += (int32_t)v[c] * (int32_t)u[c];
+                REAL sc = sV[((size_t)tap * T + t) * ng + gi] *
+                          sU[((size_t)tap * Cout + co) * ng + gi];
+                acc = FMA(sc, (REAL)P, acc);
+            }
+            Mv[tap] = acc;
+        }
+        int8_t *yq = Yqs + (size_t)s * n2;
+        REAL sy, z[16][16];
+        SUF(quantize)(Mv, 1, n2, yq, 1, &sy);
+        sYs[s] = sy;
+        for (int a = 0; a < m; ++a)
+            for (int j = 0; j < n; ++j) {
+                REAL acc = 0;
+                for (int i = 0; i < n; ++i)
+                    acc = FMA(At[a * n + i], (REAL)yq[i * n + j], acc);
+                z[a][j] = acc;
+            }
+        for (int a = 0; a < m; ++a)
+            for (int b = 0; b < m; ++b) {
+                REAL acc = 0;
+                for (int j = 0; j < n; ++j)
+                    acc = FMA(z[a][j], At[b * n + j], acc);
+                ys[((size_t)s * m + a) * m + b] = acc * sy;
+            }
+    }
+}

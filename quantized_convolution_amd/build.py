@@ -1,0 +1,47 @@
+"""Build the HIP library libwino_q8_conv.so in-tree for gfx950.
+
+One hipcc invocation compiles the kernels, the host plan and the C ABI into a
+shared library next to this file. Numerics flags: no fp contraction (every fma
+is written out), IEEE fp32 division, fp32 denormals kept.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libwino_q8_conv.so")
+SOURCES = ["wq8_kernels.hip", "wq8_plan.cpp", "wq8_api.cpp"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def build(verbose: bool = False) -> str:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    cmd = [HIPCC, *FLAGS, *srcs, "-o", LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the packed-fp32 feature; that warning is harmless
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs, file=sys.stderr)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

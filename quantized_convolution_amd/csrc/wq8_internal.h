@@ -1,0 +1,53 @@
+// Internal declarations shared by the host plan, the C ABI and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/wino_q8_conv.h"
+
+namespace wq8 {
+
+constexpr int kMaxN = 8;  // n = m + 2 for m = 6
+
+// Transform matrices passed by value to the kernels (row-major).
+struct Mats {
+    float Bt[kMaxN * kMaxN];  // [n][n]  carries S_B
+    float G[kMaxN * 3];       // [n][3]  carries S_G
+    float At[6 * kMaxN];      // [m][n]  carries S_A
+};
+
+// Problem geometry shared by every kernel.
+struct Geo {
+    int m, n, G, ng;          // tile size, n = m + 2, group size, groups per Cin
+    int N, Cin, Cout, H, W, pad;
+    int Ho, Wo, tH, tW;
+    int64_t T;                // tiles
+};
+
+// Set the thread-local error detail (printf-style) and return `st`.
+wq8_status fail(wq8_status st, const char *fmt, ...);
+void clear_error();
+
+// Kernel launchers (wq8_kernels.hip). Each returns WQ8_OK or WQ8_ERR_HIP.
+wq8_status launch_weights(const Geo &g, const Mats &mt, const float *w, int8_t *Uq, float *sU,
+                          void *stream);
+wq8_status launch_stage1(const Geo &g, const Mats &mt, wq8_dtype xdt, const void *x,
+                         int8_t *Vq, float *sV, void *stream);
+wq8_status launch_stage2(const Geo &g, const int8_t *Vq, const float *sV, const int8_t *Uq,
+                         const float *sU, float *M, int32_t *P, void *stream);
+wq8_status launch_stage3(const Geo &g, const Mats &mt, wq8_dtype ydt, const float *M, void *y,
+                         int8_t *Yq, float *sY, void *stream);
+
+}  // namespace wq8
+
+struct wq8_plan {
+    wq8::Geo geo;
+    wq8::Mats mats;
+    wq8_dtype xdt, ydt;
+    double points[wq8::kMaxN];
+    float sB[wq8::kMaxN], sG[wq8::kMaxN];
+    // forward workspace layout (bytes)
+    size_t off_vq, off_sv, off_m, ws_bytes;
+    size_t u_code_bytes, u_scale_bytes;
+};

@@ -1,0 +1,458 @@
+// Host plan: descriptor validation and the scaled Winograd transforms.
+//
+// Transforms (review page, "What carries the argument"; appendix 7.1 for the
+// Vandermonde matrix of homogeneous points):
+//   V_{a x b}[i][j] = f_i^j * g_i^(b-1-j), finite p -> (p, 1), infinity -> (1, 0)
+//   B^T = S_B V_n^-T,  G = S_G V_{n x 3},  A^T = V_{n x m}^T S_A,  S_A = (S_B S_G)^-1
+// Every entry is computed exactly as a rational with 128-bit numerator and
+// denominator (points and scales are binary floating-point numbers, hence
+// rationals) and rounded once to fp32, ties to even. An entry can sit exactly
+// on an fp32 midpoint (e.g. s * 17/18 when s carries a factor 9), so only
+// exact arithmetic decides such ties the same way every time. If a rational
+// overflows 128 bits (extreme scales or points with long binary expansions)
+// the plan falls back to Gauss-Jordan in long double, rounded once to fp32.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "wq8_internal.h"
+
+namespace wq8 {
+
+static thread_local char g_err[512];
+
+wq8_status fail(wq8_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+static const double kStd4[6] = {0.0, 1.0, -1.0, 2.0, -2.0, INFINITY};
+static const double kStd6[8] = {0.0, 1.0, -1.0, 2.0, -2.0, 0.5, -0.5, INFINITY};
+
+// Homogeneous Vandermonde row: entry j = f^j g^(cols-1-j).
+static void vrow(double p, int cols, long double *row) {
+    long double f = isinf(p) ? 1.0L : (long double)p;
+    long double g = isinf(p) ? 0.0L : 1.0L;
+    for (int j = 0; j < cols; ++j) {
+        long double v = 1.0L;
+        for (int e = 0; e < j; ++e) v *= f;
+        for (int e = 0; e < cols - 1 - j; ++e) v *= g;
+        row[j] = v;
+    }
+}
+
+// In-place inverse of the n x n matrix a (row-major); false if singular.
+static bool invert(int n, long double *a, long double *inv) {
+    long double w[kMaxN][2 * kMaxN];
+    long double amax = 0;
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < n; ++j) {
+            w[i][j] = a[i * n + j];
+            w[i][n + j] = (i == j) ? 1.0L : 0.0L;
+            if (fabsl(w[i][j]) > amax) amax = fabsl(w[i][j]);
+        }
+    for (int col = 0; col < n; ++col) {
+        int piv = col;
+        for (int r = col + 1; r < n; ++r)
+            if (fabsl(w[r][col]) > fabsl(w[piv][col])) piv = r;
+        if (!(fabsl(w[piv][col]) > 1e-12L * amax)) return false;
+        if (piv != col)
+            for (int j = 0; j < 2 * n; ++j) {
+                long double t = w[col][j];
+                w[col][j] = w[piv][j];
+                w[piv][j] = t;
+            }
+        long double p = w[col][col];
+        for (int j = 0; j < 2 * n; ++j) w[col][j] /= p;
+        for (int r = 0; r < n; ++r) {
+            if (r == col || w[r][col] == 0) continue;
+            long double f = w[r][col];
+            for (int j = 0; j < 2 * n; ++j) w[r][j] -= f * w[col][j];
+        }
+    }
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < n; ++j) inv[i * n + j] = w[i][n + j];
+    return true;
+}
+
+// ------------------------------------------------------- exact rationals
+typedef __int128 i128;
+
+struct Rat {
+    i128 num = 0, den = 1;  // den > 0, gcd(num, den) = 1
+};
+
+static i128 iabs(i128 v) { return v < 0 ? -v : v; }
+static i128 igcd(i128 a, i128 b) {
+    a = iabs(a);
+    b = iabs(b);
+    while (b) {
+        i128 t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+// All operations set *ok = false on overflow and return garbage.
+static Rat rnorm(i128 n, i128 d, bool *ok) {
+    Rat r;
+    if (d == 0) {
+        *ok = false;
+        return r;
+    }
+    if (d < 0) {
+        n = -n;
+        d = -d;
+    }
+    i128 g = igcd(n, d);
+    if (g == 0) g = 1;
+    r.num = n / g;
+    r.den = d / g;
+    return r;
+}
+static i128 mulc(i128 a, i128 b, bool *ok) {
+    i128 r;
+    if (__builtin_mul_overflow(a, b, &r)) *ok = false;
+    return r;
+}
+static Rat rmul(Rat a, Rat b, bool *ok) {
+    i128 g1 = igcd(a.num, b.den), g2 = igcd(b.num, a.den);
+    if (g1 == 0) g1 = 1;
+    if (g2 == 0) g2 = 1;
+    return rnorm(mulc(a.num / g1, b.num / g2, ok), mulc(a.den / g2, b.den / g1, ok), ok);
+}
+static Rat rinv(Rat a, bool *ok) { return rnorm(a.den, a.num, ok); }
+static Rat rsub(Rat a, Rat b, bool *ok) {
+    i128 g = igcd(a.den, b.den);
+    i128 da = a.den / g, db = b.den / g;
+    i128 n1 = mulc(a.num, db, ok), n2 = mulc(b.num, da, ok), n;
+    if (__builtin_sub_overflow(n1, n2, &n)) *ok = false;
+    return rnorm(n, mulc(a.den, db, ok), ok);
+}
+// Exact value of a finite double.
+static Rat rfrom(double v, bool *ok) {
+    if (v == 0.0) return Rat{};
+    int e;
+    double fr = frexp(v, &e);                       // v = fr * 2^e, 0.5 <= |fr| < 1
+    i128 mant = (i128)(long long)ldexp(fr, 53);      // exact 53-bit integer
+    e -= 53;
+    if (e >= 0) {
+        if (e > 70) {
+            *ok = false;
+            return Rat{};
+        }
+        return rnorm(mant << e, 1, ok);
+    }
+    if (-e > 120) {
+        *ok = false;
+        return Rat{};
+    }
+    return rnorm(mant, (i128)1 << (-e), ok);
+}
+static int bitlen(i128 v) {
+    int b = 0;
+    for (v = iabs(v); v; v >>= 1) ++b;
+    return b;
+}
+// Nearest fp32 to an exact rational, ties to even.
+static float rround(Rat q, bool *ok) {
+    if (q.num == 0) return 0.0f;
+    const bool neg = q.num < 0;
+    const i128 a = iabs(q.num), d = q.den;
+    // choose e with 2^23 <= a / (d 2^e) < 2^25, then fix to < 2^24
+    int e = bitlen(a) - bitlen(d) - 24;
+    i128 k, rem, div;
+    for (int pass = 0; pass < 2; ++pass) {
+        if (e >= 0) {
+            if (e > 100 || bitlen(d) + e > 125) {
+                *ok = false;
+                return 0.0f;
+            }
+            div = d << e;
+            k = a / div;
+            rem = a % div;
+        } else {
+            if (-e > 100 || bitlen(a) - e > 125) {
+                *ok = false;
+                return 0.0f;
+            }
+            div = d;
+            k = (a << (-e)) / d;
+            rem = (a << (-e)) % d;
+        }
+        if (k < ((i128)1 << 24)) break;
+        ++e;  // quotient had 25 bits
+    }
+    if (2 * rem > div || (2 * rem == div && (k & 1))) ++k;
+    float r = ldexpf((float)(long long)k, e);
+    if (!isfinite(r)) *ok = false;
+    return neg ? -r : r;
+}
+
+// Exact homogeneous Vandermonde row.
+static void vrow_exact(double p, int cols, Rat *row, bool *ok) {
+    Rat f, g;
+    if (isinf(p)) {
+        f = rnorm(1, 1, ok);
+        g = Rat{};
+    } else {
+        f = rfrom(p, ok);
+        g = rnorm(1, 1, ok);
+    }
+    for (int j = 0; j < cols; ++j) {
+        Rat v = rnorm(1, 1, ok);
+        for (int e = 0; e < j; ++e) v = rmul(v, f, ok);
+        for (int e = 0; e < cols - 1 - j; ++e) v = rmul(v, g, ok);
+        row[j] = v;
+    }
+}
+
+// Exact inverse by Gauss-Jordan; false if singular. *ok false on overflow.
+static bool invert_exact(int n, const Rat *a, Rat *inv, bool *ok) {
+    Rat w[kMaxN][2 * kMaxN];
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < n; ++j) {
+            w[i][j] = a[i * n + j];
+            w[i][n + j] = (i == j) ? rnorm(1, 1, ok) : Rat{};
+        }
+    for (int col = 0; col < n && *ok; ++col) {
+        int piv = -1;
+        for (int r = col; r < n; ++r)
+            if (w[r][col].num != 0) {
+                piv = r;
+                break;
+            }
+        if (piv < 0) return false;
+        if (piv != col)
+            for (int j = 0; j < 2 * n; ++j) {
+                Rat t = w[col][j];
+                w[col][j] = w[piv][j];
+                w[piv][j] = t;
+            }
+        Rat pinv = rinv(w[col][col], ok);
+        for (int j = 0; j < 2 * n; ++j) w[col][j] = rmul(w[col][j], pinv, ok);
+        for (int r = 0; r < n; ++r) {
+            if (r == col || w[r][col].num == 0) continue;
+            Rat f = w[r][col];
+            for (int j = 0; j < 2 * n; ++j) w[r][j] = rsub(w[r][j], rmul(f, w[col][j], ok), ok);
+        }
+    }
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < n; ++j) inv[i * n + j] = w[i][n + j];
+    return true;
+}
+
+// Exact construction; returns false (and leaves mt untouched) on overflow.
+static bool mats_exact(int m, const double *pts, const float *sB, const float *sG, Mats *mt,
+                       bool *singular) {
+    const int n = m + 2;
+    bool ok = true;
+    Rat vn[kMaxN * kMaxN], vinv[kMaxN * kMaxN], vr[kMaxN * 3], vm[kMaxN * 6], rb[kMaxN], rg[kMaxN];
+    for (int i = 0; i < n; ++i) {
+        vrow_exact(pts[i], n, vn + i * n, &ok);
+        vrow_exact(pts[i], 3, vr + i * 3, &ok);
+        vrow_exact(pts[i], m, vm + i * m, &ok);
+        rb[i] = rfrom(sB[i], &ok);
+        rg[i] = rfrom(sG[i], &ok);
+    }
+    if (!ok) return false;
+    if (!invert_exact(n, vn, vinv, &ok)) {
+        *singular = true;
+        return ok;
+    }
+    Mats out;
+    memset(&out, 0, sizeof out);
+    for (int i = 0; i < n; ++i) {
+        for (int k = 0; k < n; ++k) out.Bt[i * n + k] = rround(rmul(rb[i], vinv[k * n + i], &ok), &ok);
+        for (int k = 0; k < 3; ++k) out.G[i * 3 + k] = rround(rmul(rg[i], vr[i * 3 + k], &ok), &ok);
+    }
+    for (int k = 0; k < n; ++k) {
+        Rat sa = rinv(rmul(rb[k], rg[k], &ok), &ok);
+        for (int a = 0; a < m; ++a) out.At[a * n + k] = rround(rmul(vm[k * m + a], sa, &ok), &ok);
+    }
+    if (!ok) return false;
+    *mt = out;
+    return true;
+}
+
+static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+static wq8_status build(const wq8_desc *d, wq8_plan *p) {
+    if (d->m != 4 && d->m != 6)
+        return fail(WQ8_ERR_UNSUPPORTED, "m = %d: only F(4,3) and F(6,3) are built", d->m);
+    const int m = d->m, n = m + 2;
+    if (d->group != 16 && d->group != 32 && d->group != 64 && d->group != 128 && d->group != 256)
+        return fail(WQ8_ERR_UNSUPPORTED, "group = %d: must be 16, 32, 64, 128 or 256", d->group);
+    if (d->N < 1 || d->Cin < 1 || d->Cout < 1 || d->H < 1 || d->W < 1)
+        return fail(WQ8_ERR_INVALID_ARG, "sizes must be positive (N=%d Cin=%d Cout=%d H=%d W=%d)",
+                    d->N, d->Cin, d->Cout, d->H, d->W);
+    if (d->Cin % d->group != 0)
+        return fail(WQ8_ERR_INVALID_ARG, "Cin = %d is not a multiple of group = %d", d->Cin,
+                    d->group);
+    if (d->pad < 0 || d->pad > 2) return fail(WQ8_ERR_INVALID_ARG, "pad = %d: must be 0..2", d->pad);
+    if ((d->x_dtype != WQ8_F32 && d->x_dtype != WQ8_BF16) ||
+        (d->y_dtype != WQ8_F32 && d->y_dtype != WQ8_BF16))
+        return fail(WQ8_ERR_INVALID_ARG, "unknown dtype");
+    Geo &g = p->geo;
+    g.m = m;
+    g.n = n;
+    g.G = d->group;
+    g.ng = d->Cin / d->group;
+    g.N = d->N;
+    g.Cin = d->Cin;
+    g.Cout = d->Cout;
+    g.H = d->H;
+    g.W = d->W;
+    g.pad = d->pad;
+    g.Ho = d->H + 2 * d->pad - 2;
+    g.Wo = d->W + 2 * d->pad - 2;
+    if (g.Ho < 1 || g.Wo < 1)
+        return fail(WQ8_ERR_INVALID_ARG, "empty output: H=%d W=%d pad=%d", d->H, d->W, d->pad);
+    g.tH = (g.Ho + m - 1) / m;
+    g.tW = (g.Wo + m - 1) / m;
+    g.T = (int64_t)g.N * g.tH * g.tW;
+    // every buffer must be addressable with 64-bit offsets and the
+    // per-tap planes with 32-bit element counts inside a kernel
+    const int64_t n2 = (int64_t)n * n;
+    const int64_t lim = (int64_t)1 << 31;
+    if (g.T * d->Cin >= lim || g.T * d->Cout >= lim || (int64_t)d->Cout * d->Cin >= lim ||
+        (int64_t)d->N * d->Cin * d->H * d->W >= lim * 4 ||
+        (int64_t)d->N * d->Cout * g.Ho * g.Wo >= lim * 4)
+        return fail(WQ8_ERR_UNSUPPORTED, "problem too large for this build");
+    p->xdt = d->x_dtype;
+    p->ydt = d->y_dtype;
+
+    // points and scales
+    const double *pts = d->points ? d->points : (m == 4 ? kStd4 : kStd6);
+    int ninf = 0;
+    for (int i = 0; i < n; ++i) {
+        double v = pts[i];
+        if (isnan(v) || (isinf(v) && v < 0))
+            return fail(WQ8_ERR_INVALID_ARG, "point %d is not a number or +infinity", i);
+        ninf += isinf(v) ? 1 : 0;
+        p->points[i] = v;
+        float sb = d->s_B ? d->s_B[i] : 1.0f;
+        float sg = d->s_G ? d->s_G[i] : 1.0f;
+        if (!isfinite(sb) || !isfinite(sg) || sb == 0.0f || sg == 0.0f)
+            return fail(WQ8_ERR_INVALID_ARG, "scale %d must be finite and non-zero", i);
+        p->sB[i] = sb;
+        p->sG[i] = sg;
+    }
+    for (int i = 0; i < n; ++i)
+        for (int j = i + 1; j < n; ++j)
+            if (pts[i] == pts[j]) return fail(WQ8_ERR_SINGULAR_POINTS, "points %d and %d coincide", i, j);
+    if (ninf > 1) return fail(WQ8_ERR_SINGULAR_POINTS, "more than one point at infinity");
+
+    Mats &mt = p->mats;
+    bool singular = false;
+    if (!mats_exact(m, pts, p->sB, p->sG, &mt, &singular)) {
+        // rationals overflowed 128 bits: long double Gauss-Jordan instead
+        long double vn[kMaxN * kMaxN], vinv[kMaxN * kMaxN], vr[kMaxN * 3], vm[kMaxN * 6];
+        for (int i = 0; i < n; ++i) {
+            vrow(pts[i], n, vn + i * n);
+            vrow(pts[i], 3, vr + i * 3);
+            vrow(pts[i], m, vm + i * m);
+        }
+        if (!invert(n, vn, vinv))
+            return fail(WQ8_ERR_SINGULAR_POINTS, "Vandermonde matrix of the points is singular");
+        memset(&mt, 0, sizeof mt);
+        for (int i = 0; i < n; ++i) {
+            const long double sb = p->sB[i], sg = p->sG[i];
+            for (int k = 0; k < n; ++k) mt.Bt[i * n + k] = (float)(sb * vinv[k * n + i]);
+            for (int k = 0; k < 3; ++k) mt.G[i * 3 + k] = (float)(sg * vr[i * 3 + k]);
+        }
+        for (int a = 0; a < m; ++a)
+            for (int k = 0; k < n; ++k) {
+                const long double sa = 1.0L / ((long double)p->sB[k] * (long double)p->sG[k]);
+                mt.At[a * n + k] = (float)(vm[k * m + a] * sa);
+            }
+    } else if (singular) {
+        return fail(WQ8_ERR_SINGULAR_POINTS, "Vandermonde matrix of the points is singular");
+    }
+    for (int i = 0; i < n * n; ++i)
+        if (!isfinite(mt.Bt[i])) return fail(WQ8_ERR_INVALID_ARG, "B^T overflows fp32");
+    for (int i = 0; i < m * n; ++i)
+        if (!isfinite(mt.At[i])) return fail(WQ8_ERR_INVALID_ARG, "A^T overflows fp32");
+    for (int i = 0; i < n * 3; ++i)
+        if (!isfinite(mt.G[i])) return fail(WQ8_ERR_INVALID_ARG, "G overflows fp32");
+
+    // workspace: Vq | sV | M, each 256-byte aligned
+    p->off_vq = 0;
+    p->off_sv = round_up((size_t)(n2 * g.T * g.Cin), 256);
+    p->off_m = p->off_sv + round_up((size_t)(n2 * g.T * g.ng) * 4, 256);
+    p->ws_bytes = p->off_m + (size_t)(n2 * g.T * g.Cout) * 4;
+    p->u_code_bytes = (size_t)(n2 * g.Cout * g.Cin);
+    p->u_scale_bytes = (size_t)(n2 * g.Cout * g.ng) * 4;
+    return WQ8_OK;
+}
+
+}  // namespace wq8
+
+extern "C" {
+
+wq8_status wq8_plan_create(const wq8_desc *desc, wq8_plan **out) {
+    wq8::clear_error();
+    if (!desc || !out) return wq8::fail(WQ8_ERR_INVALID_ARG, "null descriptor or output pointer");
+    *out = nullptr;
+    wq8_plan *p = new (std::nothrow) wq8_plan;
+    if (!p) return wq8::fail(WQ8_ERR_NO_MEMORY, "plan allocation failed");
+    memset(p, 0, sizeof *p);
+    wq8_status st = wq8::build(desc, p);
+    if (st != WQ8_OK) {
+        delete p;
+        return st;
+    }
+    *out = p;
+    return WQ8_OK;
+}
+
+void wq8_plan_destroy(wq8_plan *plan) { delete plan; }
+
+wq8_status wq8_plan_query(const wq8_plan *p, size_t *ws, size_t *ucode, size_t *uscale,
+                          int64_t *tiles) {
+    wq8::clear_error();
+    if (!p) return wq8::fail(WQ8_ERR_INVALID_ARG, "null plan");
+    if (ws) *ws = p->ws_bytes;
+    if (ucode) *ucode = p->u_code_bytes;
+    if (uscale) *uscale = p->u_scale_bytes;
+    if (tiles) *tiles = p->geo.T;
+    return WQ8_OK;
+}
+
+wq8_status wq8_plan_matrices(const wq8_plan *p, float *Bt, float *G, float *At) {
+    wq8::clear_error();
+    if (!p) return wq8::fail(WQ8_ERR_INVALID_ARG, "null plan");
+    const int n = p->geo.n, m = p->geo.m;
+    if (Bt) memcpy(Bt, p->mats.Bt, sizeof(float) * n * n);
+    if (G) memcpy(G, p->mats.G, sizeof(float) * n * 3);
+    if (At) memcpy(At, p->mats.At, sizeof(float) * m * n);
+    return WQ8_OK;
+}
+
+const char *wq8_status_string(wq8_status s) {
+    switch (s) {
+        case WQ8_OK: return "ok";
+        case WQ8_ERR_INVALID_ARG: return "invalid argument";
+        case WQ8_ERR_UNSUPPORTED: return "unsupported configuration";
+        case WQ8_ERR_SINGULAR_POINTS: return "interpolation points are not distinct";
+        case WQ8_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case WQ8_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+        case WQ8_ERR_HIP: return "HIP error";
+        case WQ8_ERR_NO_MEMORY: return "out of host memory";
+    }
+    return "unknown status";
+}
+
+const char *wq8_last_error(void) { return wq8::g_err; }
+
+}  // extern "C"

@@ -1,0 +1,226 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bars (floating point decides the int8 codes, so both sides take those
+decisions in fp32 with the same operation order):
+  * int8 codes (Uq, Vq, Yq): mismatches in at most 1e-4 of the values, each at
+    most one step (a rounding tie); in practice they are identical;
+  * int32 Hadamard partials given identical codes: bit-exact;
+  * group and tile scales: identical wherever the codes agree;
+  * outputs: max |gpu - oracle| <= 1e-3 * RMS(oracle output).
+Inputs come from quantized_convolution_amd.workloads (seeded) and the oracle
+only ever sees those inputs, never a GPU result.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_convolution_amd as q
+from quantized_convolution_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+CODE_MISMATCH_MAX = 1e-4
+OUT_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q.load()
+    return torch.device("cuda:0")
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.asarray(a, np.float64) ** 2)))
+
+
+def assert_codes(got, ref, what):
+    got, ref = np.asarray(got), np.asarray(ref)
+    assert got.shape == ref.shape, what
+    bad = got != ref
+    frac = float(bad.mean()) if bad.size else 0.0
+    if bad.any():
+        step = np.abs(got.astype(np.int32) - ref.astype(np.int32))[bad].max()
+        assert step <= 1, f"{what}: code differs by {step}"
+    assert frac <= CODE_MISMATCH_MAX, f"{what}: {frac:.2e} of codes differ"
+    return frac
+
+
+def assert_out(got, ref, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, what
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    assert err <= OUT_TOL * rms(ref) or err == 0.0, f"{what}: max err {err:.3e}, rms {rms(ref):.3e}"
+    return err
+
+
+def make_plan(L, d, xdt=torch.float32, ydt=None):
+    return q.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"], s_B=d["s_b"],
+                  s_G=d["s_g"], x_dtype=xdt, y_dtype=ydt)
+
+
+def to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+# ------------------------------------------------------------ small sizes
+SMALL = [WL.small(L) for L in WL.LAYERS.values()]
+EDGE = [
+    WL.LAYERS["c1_f4_n1_c16_16x16_g16"],                                      # full c1
+    WL.small(WL.LAYERS["c1_f4_n1_c16_16x16_g16"], H=1, W=1),                  # 1x1 image
+    WL.small(WL.LAYERS[WL.BENCH_LAYER], H=3, W=70, Cin=64, Cout=13),          # odd Cout, wide
+    WL.small(WL.LAYERS[WL.BENCH_LAYER], N=3, H=7, W=6, Cin=64, Cout=1),       # Cout = 1
+    WL.small(WL.LAYERS[WL.BENCH_LAYER], H=12, W=12).replace(pad=0, name="pad0"),
+    WL.small(WL.LAYERS[WL.BENCH_LAYER], H=5, W=9).replace(pad=2, name="pad2"),
+    WL.small(WL.LAYERS["c5_f6_n8_c1280_16x16_g128"], Cin=256, Cout=40).replace(G=256, name="g256"),
+    WL.small(WL.LAYERS["c5_f6_n8_c640_32x32_g32"], Cin=96, Cout=20, H=14, W=14),  # 3 groups
+    WL.small(WL.LAYERS["c4_f4_n2_c320_64x64_g64_pert"], N=2, Cin=192, Cout=70, H=21, W=19),
+]
+
+
+def ids(Ls):
+    return [L.name for L in Ls]
+
+
+@pytest.mark.parametrize("L", SMALL + EDGE, ids=ids(SMALL + EDGE))
+def test_stages_and_forward(dev, L):
+    print(f"\n[case] {L.name} F({L.m},3) N={L.N} C={L.Cin}->{L.Cout} {L.H}x{L.W} pad={L.pad} "
+          f"G={L.G}", flush=True)
+    d = WL.make(L)
+    ref = oracle.forward(L.m, d["x"], d["w"], L.pad, L.G, points=list(d["points"]), s_b=d["s_b"],
+                         s_g=d["s_g"], keep=True)
+    plan = make_plan(L, d)
+    # matrices
+    Bt, Gm, At = q.wq8_plan_matrices(plan)
+    assert np.array_equal(Bt, ref["Bt"]) and np.array_equal(Gm, ref["G"])
+    assert np.array_equal(At, ref["At"])
+    # weights
+    Uq, sU = q.wq8_weights_prepare(plan, to_dev(d["w"], dev))
+    torch.cuda.synchronize()
+    assert_codes(Uq.cpu().numpy(), ref["Uq"], "Uq")
+    assert np.array_equal(sU.cpu().numpy(), ref["sU"])
+    # stage 1
+    Vq, sV = q.wq8_stage1(plan, to_dev(d["x"], dev))
+    torch.cuda.synchronize()
+    assert_codes(Vq.cpu().numpy(), ref["Vq"], "Vq")
+    assert np.array_equal(sV.cpu().numpy(), ref["sV"])
+    # stage 2 from the oracle's codes: int32 partials exact, M exact
+    oVq, oUq = to_dev(ref["Vq"], dev), to_dev(ref["Uq"], dev)
+    P = q.wq8_stage2_i32(plan, oVq, oUq)
+    M = q.wq8_stage2(plan, oVq, to_dev(ref["sV"], dev), oUq, to_dev(ref["sU"], dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(P.cpu().numpy(), oracle.stage2_i32(ref["Vq"], ref["Uq"], L.G))
+    assert np.array_equal(M.cpu().numpy(), ref["M"])
+    # stage 3 from the oracle's M
+    y3, Yq, sY = q.wq8_stage3(plan, to_dev(ref["M"], dev), want_codes=True)
+    torch.cuda.synchronize()
+    assert_codes(Yq.cpu().numpy(), ref["Yq"], "Yq")
+    assert np.array_equal(sY.cpu().numpy(), ref["sY"])
+    assert_out(y3.cpu().numpy(), ref["y"], "stage-3 output")
+    # whole forward
+    y = q.wq8_conv_forward(plan, to_dev(d["x"], dev), Uq, sU)
+    torch.cuda.synchronize()
+    err = assert_out(y.cpu().numpy(), ref["y"], "forward")
+    print(f"[case] {L.name}: forward max err {err:.3e} (rms {rms(ref['y']):.3e})", flush=True)
+
+
+@pytest.mark.parametrize("xdt,ydt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.bfloat16),
+                                     (torch.bfloat16, torch.float32)])
+def test_bf16_activations(dev, xdt, ydt):
+    L = WL.small(WL.LAYERS[WL.BENCH_LAYER], N=2, H=15, W=13, Cin=64, Cout=24)
+    print(f"\n[case] bf16 {xdt} -> {ydt} {L.name}", flush=True)
+    d = WL.make(L)
+    xt = torch.from_numpy(d["x"]).to(xdt)
+    x_ref = d["x"] if xdt == torch.float32 else oracle.bf16_bits_to_f32(
+        xt.view(torch.int16).numpy().view(np.uint16))
+    ref = oracle.forward(L.m, x_ref, d["w"], L.pad, L.G, points=list(d["points"]), s_b=d["s_b"],
+                         s_g=d["s_g"])
+    plan = make_plan(L, d, xdt, ydt)
+    Uq, sU = q.wq8_weights_prepare(plan, to_dev(d["w"], dev))
+    y = q.wq8_conv_forward(plan, xt.to(dev), Uq, sU)
+    torch.cuda.synchronize()
+    if ydt == torch.bfloat16:
+        bits = y.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(bits, oracle.f32_to_bf16_bits(ref))
+    else:
+        assert_out(y.cpu().numpy(), ref, "bf16-in forward")
+
+
+def test_zero_input_gives_zero_scales(dev):
+    L = WL.small(WL.LAYERS[WL.BENCH_LAYER], N=1, H=9, W=9, Cin=64, Cout=16)
+    d = WL.make(L)
+    plan = make_plan(L, d)
+    x = torch.zeros((L.N, L.Cin, L.H, L.W), device=dev)
+    Uq, sU = q.wq8_weights_prepare(plan, to_dev(d["w"], dev))
+    Vq, sV = q.wq8_stage1(plan, x)
+    y = q.wq8_conv_forward(plan, x, Uq, sU)
+    torch.cuda.synchronize()
+    assert not Vq.any() and not sV.any() and not y.any()
+
+
+def test_forward_is_deterministic(dev):
+    L = WL.LAYERS["c3a_f6_n32_c128_28x28_g64"]
+    d = WL.make(L)
+    plan = make_plan(L, d)
+    Uq, sU = q.wq8_weights_prepare(plan, to_dev(d["w"], dev))
+    x = to_dev(d["x"], dev)
+    ws = plan.empty_workspace(dev)
+    a = q.wq8_conv_forward(plan, x, Uq, sU, workspace=ws).clone()
+    ws.fill_(0x5A)
+    b = q.wq8_conv_forward(plan, x, Uq, sU, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+# ------------------------------------------------------------- full sizes
+FULL = list(WL.LAYERS.values())
+
+
+@pytest.mark.parametrize("L", FULL, ids=ids(FULL))
+def test_full_size_sampled(dev, L):
+    """Full configuration, launched exactly as the benchmark launches it
+    (wq8_conv_forward with a plan-sized workspace). Transforms and codes are
+    compared in full; the Hadamard stage, Y codes and outputs at 192 sampled
+    (tile, co) pairs that the oracle evaluates one by one."""
+    print(f"\n[case] full {L.name}", flush=True)
+    d = WL.make(L)
+    from oracle import transforms as T
+    Bt, Gm, At = T.transforms_f32(L.m, list(d["points"]), d["s_b"], d["s_g"])
+    oUq, osU = oracle.weights(L.m, d["w"], L.G, Gm)
+    oVq, osV = oracle.stage1(L.m, d["x"], L.pad, L.G, Bt)
+    plan = make_plan(L, d)
+    x = to_dev(d["x"], dev)
+    Uq, sU = q.wq8_weights_prepare(plan, to_dev(d["w"], dev))
+    y = q.wq8_conv_forward(plan, x, Uq, sU, workspace=plan.empty_workspace(dev))
+    Vq, sV = q.wq8_stage1(plan, x)
+    torch.cuda.synchronize()
+    fu = assert_codes(Uq.cpu().numpy(), oUq, "Uq")
+    fv = assert_codes(Vq.cpu().numpy(), oVq, "Vq")
+    if fu == 0 and fv == 0:
+        assert np.array_equal(sU.cpu().numpy(), osU) and np.array_equal(sV.cpu().numpy(), osV)
+    r = np.random.default_rng([L.cfg_id, L.layer_idx, 99])
+    S = 192
+    pairs = np.stack([r.integers(0, plan.T, S), r.integers(0, L.Cout, S)], 1)
+    pairs[0] = (plan.T - 1, L.Cout - 1)          # the ragged corner
+    Ms, Yqs, sYs, ys = oracle.sampled(L.m, oVq, osV, oUq, osU, At, pairs)
+    M = q.wq8_stage2(plan, Vq, sV, Uq, sU)
+    torch.cuda.synchronize()
+    Mg = M.cpu().numpy()[:, pairs[:, 0], pairs[:, 1]].T
+    if fu == 0 and fv == 0:
+        assert np.array_equal(Mg, Ms)
+    yg = y.cpu().numpy()
+    tH, tW = -(-L.Ho // L.m), -(-L.Wo // L.m)
+    got, want = [], []
+    for s, (t, co) in enumerate(pairs):
+        img, ty, tx = t // (tH * tW), t // tW % tH, t % tW
+        blk = yg[img, co, ty * L.m:(ty + 1) * L.m, tx * L.m:(tx + 1) * L.m]
+        got.append(blk.reshape(-1))
+        want.append(ys[s][:blk.shape[0], :blk.shape[1]].reshape(-1))
+    got, want = np.concatenate(got), np.concatenate(want)
+    # RMS of the whole oracle output is estimated from the sampled tiles
+    err = float(np.max(np.abs(got.astype(np.float64) - want)))
+    assert err <= OUT_TOL * rms(want), f"max err {err:.3e} rms {rms(want):.3e}"
+    print(f"[case] full {L.name}: sampled max err {err:.3e}", flush=True)

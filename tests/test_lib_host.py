@@ -1,0 +1,142 @@
+"""Host-side checks of the HIP library: it loads, exports every entry point the
+header declares, validates descriptors, and builds the same fp32 transform
+matrices as the oracle's exact construction. No kernel is launched."""
+import ctypes as C
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import transforms as T
+from quantized_convolution_amd import binding as B
+from quantized_convolution_amd import workloads as WL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HAS_GPU = torch.cuda.is_available()
+
+
+def header_functions():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(wq8_\w+)\s*\(", src))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    declared = header_functions()
+    assert len(declared) >= 12
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(B.EXPORTS)
+
+
+def _create(**kw):
+    base = dict(m=6, points=None, s_B=None, s_G=None, group=64, N=1, Cin=64, Cout=64, H=16, W=16,
+                pad=1, x_dtype=0, y_dtype=0)
+    base.update(kw)
+    keep = []
+
+    def arr(v, ct, dt):
+        if v is None:
+            return None
+        a = np.ascontiguousarray(v, dtype=dt)
+        keep.append(a)
+        return a.ctypes.data_as(C.POINTER(ct))
+
+    d = B.wq8_desc(base["m"], arr(base["points"], C.c_double, np.float64),
+                   arr(base["s_B"], C.c_float, np.float32), arr(base["s_G"], C.c_float, np.float32),
+                   base["group"], base["N"], base["Cin"], base["Cout"], base["H"], base["W"],
+                   base["pad"], base["x_dtype"], base["y_dtype"])
+    h = C.c_void_p()
+    st = B.wq8_plan_create(d, h)
+    if st == 0:
+        B.load().wq8_plan_destroy(h)
+    return st
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, 0),
+    (dict(m=4), 0),
+    (dict(m=5), -2), (dict(m=2), -2),
+    (dict(group=48), -2), (dict(group=8), -2),
+    (dict(Cin=96, group=64), -1), (dict(Cin=96, group=32), 0),
+    (dict(pad=3), -1), (dict(pad=-1), -1),
+    (dict(H=1, W=1, pad=0), -1), (dict(H=1, W=1, pad=1), 0),
+    (dict(N=0), -1), (dict(Cout=0), -1),
+    (dict(x_dtype=7), -1),
+    (dict(points=[0, 1, -1, 2, 2, .5, -.5, math.inf]), -3),
+    (dict(points=[0, 1, -1, 2, -2, .5, math.inf, math.inf]), -3),
+    (dict(points=[0, 1, -1, 2, -2, .5, -.5, math.nan]), -1),
+    (dict(s_B=[1, 1, 0, 1, 1, 1, 1, 1]), -1),
+    (dict(s_G=[1, 1, 1, 1, math.inf, 1, 1, 1]), -1),
+    (dict(s_B=[3e38] * 8, s_G=[1e-3] * 8), -1),
+    (dict(N=4096, Cin=1024, Cout=1024, H=512, W=512, group=64), -2),
+])
+def test_plan_validation(kw, status):
+    assert _create(**kw) == status
+
+
+def test_last_error_names_the_problem():
+    assert _create(group=48) == -2
+    assert b"group" in B.load().wq8_last_error()
+    assert B.load().wq8_status_string(-4) == b"workspace too small"
+
+
+def _scale_sets():
+    sets = [("identity", np.ones(8, np.float32), np.ones(8, np.float32))]
+    for name, L in WL.LAYERS.items():
+        if L.m == 6 and L.scales == "perturbed":
+            sb, sg = WL.make_scales(L)
+            sets.append((name, sb, sg))
+    r = np.random.default_rng(77)
+    for k in range(20):
+        sets.append((f"rand{k}", np.exp(r.uniform(-2, 2, 8)).astype(np.float32) * r.choice([-1, 1], 8),
+                     np.exp(r.uniform(-2, 2, 8)).astype(np.float32)))
+    return sets
+
+
+@pytest.mark.parametrize("m", [4, 6])
+def test_plan_matrices_equal_exactly_rounded(m):
+    n = m + 2
+    for name, sb, sg in _scale_sets():
+        sb, sg = sb[:n], sg[:n]
+        plan = B.Plan(m, 1, 16, 16, 9, 9, 1, 16, s_B=sb, s_G=sg)
+        Bt, Gm, At = B.wq8_plan_matrices(plan)
+        rb, rg, ra = T.transforms_f32(m, T.standard_points(m), sb, sg)
+        assert np.array_equal(Bt, rb), name
+        assert np.array_equal(Gm, rg), name
+        assert np.array_equal(At, ra), name
+
+
+def test_plan_query_sizes():
+    L = WL.LAYERS[WL.BENCH_LAYER]
+    plan = B.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G)
+    n2 = L.n ** 2
+    assert plan.T == L.tiles == 3200
+    assert plan.u_code_bytes == n2 * L.Cout * L.Cin
+    assert plan.u_scale_bytes == n2 * L.Cout * (L.Cin // L.G) * 4
+    assert plan.workspace_bytes >= n2 * plan.T * (L.Cin + 4 * (L.Cin // L.G) + 4 * L.Cout)
+
+
+@pytest.mark.skipif(HAS_GPU, reason="host-only argument checks; uses fake device pointers")
+def test_forward_rejects_bad_arguments_before_launch():
+    lib = B.load()
+    plan = B.Plan(6, 1, 64, 64, 16, 16, 1, 64)
+    h = plan.handle
+    good = C.c_void_p(0x10000)
+    ws = plan.workspace_bytes
+    f = lib.wq8_conv_forward
+    assert f(None, good, good, good, C.c_void_p(0x20000), good, ws, None) == -1
+    assert f(h, None, good, good, C.c_void_p(0x20000), good, ws, None) == -1
+    assert f(h, C.c_void_p(0x10004), good, good, C.c_void_p(0x20000), good, ws, None) == -5
+    assert f(h, good, good, good, C.c_void_p(0x20000), good, ws - 1, None) == -4
+    assert f(h, good, good, good, good, C.c_void_p(0x30000), ws, None) == -1   # x == y
+    assert lib.wq8_stage3(h, good, None, None, None, None) == -1
+    assert lib.wq8_stage3(h, good, good, C.c_void_p(0x40008), None, None) == -5

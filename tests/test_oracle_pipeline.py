@@ -375,3 +375,26 @@ def test_bf16_helpers_match_torch():
     assert np.array_equal(bits, ref)
     back = oracle.bf16_bits_to_f32(bits)
     assert np.array_equal(back, torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+# ------------------------------------------------ sampled evaluation
+@pytest.mark.parametrize("m,G", [(6, 16), (4, 32)])
+def test_sampled_equals_full_pipeline(m, G):
+    # the per-pair evaluation must reproduce the full stages bit for bit
+    x, w = rand_layer(31, 2, 64, 24, 2 * m + 5, 3 * m - 1)
+    sb, sg = pert_scales(31, m + 2)
+    q = oracle.forward(m, x, w, 1, G, s_b=sb, s_g=sg, keep=True)
+    T_ = q["M"].shape[1]
+    r = np.random.default_rng(3)
+    pairs = np.stack([r.integers(0, T_, 40), r.integers(0, 24, 40)], 1)
+    Ms, Yq, sY, ys = oracle.sampled(m, q["Vq"], q["sV"], q["Uq"], q["sU"], q["At"], pairs)
+    assert np.array_equal(Ms, q["M"][:, pairs[:, 0], pairs[:, 1]].T)
+    assert np.array_equal(Yq, q["Yq"][pairs[:, 0], pairs[:, 1]])
+    assert np.array_equal(sY, q["sY"][pairs[:, 0], pairs[:, 1]])
+    N, _, H, W = x.shape
+    Ho, Wo = H, W
+    tH, tW = -(-Ho // m), -(-Wo // m)
+    for s, (t, co) in enumerate(pairs):
+        img, ty, tx = t // (tH * tW), t // tW % tH, t % tW
+        blk = q["y"][img, co, ty * m:(ty + 1) * m, tx * m:(tx + 1) * m]
+        assert np.array_equal(ys[s][:blk.shape[0], :blk.shape[1]], blk)
