@@ -41,7 +41,8 @@ def stage_bytes(L, plan):
     vq, sv = n2 * T * L.Cin, n2 * T * ng * 4
     uq, su = n2 * L.Cout * L.Cin, n2 * L.Cout * ng * 4
     mb = n2 * T * L.Cout * 4
-    return {"stage1": xb + vq + sv, "stage2": vq + sv + uq + su + mb, "stage3": mb + yb}
+    return {"stage1": xb + vq + sv, "stage2": vq + sv + uq + su + mb, "stage3": mb + yb,
+            "stage23": vq + sv + uq + su + yb}
 
 
 def time_events(fn, iters, stream):
@@ -80,24 +81,10 @@ def cpu_baseline(L, d, min_seconds=10.0):
                       f"{t * 1e3:.1f} ms each"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--layer", default=WL.BENCH_LAYER, choices=sorted(WL.LAYERS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is not "
-              "sharded across GPUs in this build", file=sys.stderr)
-        sys.exit(2)
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    L = WL.LAYERS[args.layer]
+def run_layer(L, algo, steps, warmup, dev):
     d = WL.make(L)
     plan = q.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"],
-                  s_B=d["s_b"], s_G=d["s_g"])
+                  s_B=d["s_b"], s_G=d["s_g"], algo=algo)
     x = torch.from_numpy(d["x"]).to(dev)
     w = torch.from_numpy(d["w"]).to(dev)
     Uq, sU = q.wq8_weights_prepare(plan, w)
@@ -108,53 +95,90 @@ def main():
     def step():
         q.wq8_conv_forward(plan, x, Uq, sU, y=y, workspace=ws)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = time_events(step, args.steps, stream)
+    ms = time_events(step, steps, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    tops = L.direct_ops() / (ms * 1e-3) / 1e12
 
     # per-kernel durations: each stage entry point launches exactly the kernel
     # the forward launches, with the same grid, on the same stream
     n2 = plan.n ** 2
     Vq = torch.empty((n2, plan.T, L.Cin), dtype=torch.int8, device=dev)
     sV = torch.empty((n2, plan.T, plan.ng), dtype=torch.float32, device=dev)
-    M = torch.empty((n2, plan.T, L.Cout), dtype=torch.float32, device=dev)
-    iters = max(20, args.steps // 2)
-    k_ms = {
-        "stage1": time_events(lambda: q.wq8_stage1(plan, x, Vq, sV), iters, stream),
-        "stage2": time_events(lambda: q.wq8_stage2(plan, Vq, sV, Uq, sU, M), iters, stream),
-        "stage3": time_events(lambda: q.wq8_stage3(plan, M, y), iters, stream),
-    }
+    iters = max(20, steps // 2)
+    k_ms = {"stage1": time_events(lambda: q.wq8_stage1(plan, x, Vq, sV), iters, stream)}
+    if plan.fused:
+        k_ms["stage23"] = time_events(lambda: q.wq8_stage23(plan, Vq, sV, Uq, sU, y), iters, stream)
+    else:
+        M = torch.empty((n2, plan.T, L.Cout), dtype=torch.float32, device=dev)
+        k_ms["stage2"] = time_events(lambda: q.wq8_stage2(plan, Vq, sV, Uq, sU, M), iters, stream)
+        k_ms["stage3"] = time_events(lambda: q.wq8_stage3(plan, M, y), iters, stream)
     nbytes = stage_bytes(L, plan)
+    hop = 2 * n2 * plan.T * L.Cin * L.Cout
+    stages = {}
+    for k, v in k_ms.items():
+        gbs = nbytes[k] / (v * 1e-3) / 1e9
+        stages[k] = {"us": round(v * 1e3, 2), "GB_s": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if k in ("stage2", "stage23"):
+            stages[k]["int8_TOPS"] = round(hop / (v * 1e-3) / 1e12, 2)
+            stages[k]["mfma_frac"] = round(hop / (v * 1e-3) / 1e12 / INT8_PEAK_TOPS, 5)
     dom = max(k_ms, key=k_ms.get)
     achieved = nbytes[dom] / (k_ms[dom] * 1e-3) / 1e9
-    stages = {k: {"us": round(v * 1e3, 2), "GB_s": round(nbytes[k] / (v * 1e-3) / 1e9, 1),
-                  "hbm_frac": round(nbytes[k] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-              for k, v in k_ms.items()}
-    hop = 2 * n2 * plan.T * L.Cin * L.Cout
-    stages["stage2"]["int8_TOPS"] = round(hop / (k_ms["stage2"] * 1e-3) / 1e12, 2)
-    stages["stage2"]["mfma_frac"] = round(hop / (k_ms["stage2"] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 5)
+    return dict(plan=plan, d=d, ms=ms, wall=wall, stages=stages, dom=dom, achieved=achieved,
+                nbytes=nbytes, tops=L.direct_ops() / (ms * 1e-3) / 1e12)
 
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layer", default=WL.BENCH_LAYER, choices=sorted(WL.LAYERS))
+    ap.add_argument("--algo", default="auto", choices=["auto", "staged", "fused"])
+    ap.add_argument("--sweep", action="store_true",
+                    help="one line per layer and schedule (for tuning; no CPU baseline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is not "
+              "sharded across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    if args.sweep:
+        for name, L in WL.LAYERS.items():
+            for algo in ("staged", "fused"):
+                r = run_layer(L, algo, args.steps, args.warmup, dev)
+                print(json.dumps({"layer": name, "algo": algo, "us": round(r["ms"] * 1e3, 2),
+                                  "TOPS": round(r["tops"], 2), "stages": r["stages"]}), flush=True)
+        return
+
+    L = WL.LAYERS[args.layer]
+    r = run_layer(L, args.algo, args.steps, args.warmup, dev)
+    plan, dom = r["plan"], r["dom"]
     out = {
         "metric": "direct-conv-equiv int8 TOPS per layer, F(6,3); % MFMA int8 peak + HBM GB/s",
-        "value": round(tops, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "value": round(r["tops"], 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["ms"], 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": L.name, "m": L.m, "N": L.N, "Cin": L.Cin, "Cout": L.Cout,
                    "H": L.H, "W": L.W, "pad": L.pad, "group": L.G, "scales": L.scales,
-                   "x_dtype": "f32", "tiles": plan.T},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": nbytes[dom]},
-        "stages": stages,
-        "wall_s": round(wall, 3),
+                   "x_dtype": "f32", "tiles": plan.T,
+                   "schedule": "fused" if plan.fused else "staged"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(r["achieved"], 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(r["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": r["nbytes"][dom]},
+        "stages": r["stages"],
+        "wall_s": round(r["wall"], 3),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(L, d)
+        out["cpu_baseline"] = cpu_baseline(L, r["d"])
     print(json.dumps(out), flush=True)
 
 

@@ -70,6 +70,15 @@ typedef enum {
 
 typedef enum { WQ8_F32 = 0, WQ8_BF16 = 1 } wq8_dtype;
 
+/* How wq8_conv_forward runs stages 2 and 3 (same results either way):
+ *   STAGED: an int8 GEMM kernel writes M (fp32) to the workspace and a second
+ *           kernel requantizes it and applies the output transform;
+ *   FUSED:  one kernel keeps M on chip (LDS/registers) per 16 tiles x 16
+ *           output channels, re-reading the prepared weights per tile block;
+ *   AUTO:   FUSED when the weights are small enough that re-reading them
+ *           costs less than writing and reading M, else STAGED. */
+typedef enum { WQ8_ALGO_AUTO = 0, WQ8_ALGO_STAGED = 1, WQ8_ALGO_FUSED = 2 } wq8_algo;
+
 typedef struct wq8_plan wq8_plan; /* opaque */
 
 typedef struct {
@@ -84,18 +93,22 @@ typedef struct {
     int pad;               /* 0, 1 or 2 */
     wq8_dtype x_dtype;     /* activations in */
     wq8_dtype y_dtype;     /* activations out */
+    wq8_algo algo;         /* stage 2 + 3 schedule for wq8_conv_forward */
 } wq8_desc;
 
 /* Validates the descriptor and builds the scaled transforms on the host (exact
- * to long double, rounded once to fp32). No device work. The caller owns *out
- * and frees it with wq8_plan_destroy. */
+ * rational arithmetic, each entry rounded once to fp32, ties to even). No
+ * device work. The caller owns *out and frees it with wq8_plan_destroy. */
 wq8_status wq8_plan_create(const wq8_desc *desc, wq8_plan **out);
 void wq8_plan_destroy(wq8_plan *plan);
 
-/* Sizes in bytes of the forward workspace and of the prepared weights, and the
- * tile count T. Any output pointer may be NULL. */
+/* Sizes in bytes of the forward workspace (for the schedule the plan chose)
+ * and of the prepared weights, the tile count T, and the schedule itself
+ * (WQ8_ALGO_STAGED or WQ8_ALGO_FUSED, never AUTO). Any output pointer may be
+ * NULL. */
 wq8_status wq8_plan_query(const wq8_plan *plan, size_t *workspace_bytes,
-                          size_t *u_code_bytes, size_t *u_scale_bytes, int64_t *tiles);
+                          size_t *u_code_bytes, size_t *u_scale_bytes, int64_t *tiles,
+                          wq8_algo *algo);
 
 /* Host copies of the fp32 matrices the kernels use: Bt [n][n] (carries S_B),
  * G [n][3] (carries S_G), At [m][n] (carries S_A). Any pointer may be NULL. */
@@ -128,6 +141,11 @@ wq8_status wq8_stage2_i32(const wq8_plan *plan, const int8_t *Vq, const int8_t *
  * optional outputs (NULL to skip). */
 wq8_status wq8_stage3(const wq8_plan *plan, const float *M, void *y, int8_t *Yq,
                       float *sY, void *stream);
+
+/* Stages 2 and 3 as the single fused kernel (M stays on chip): the same y as
+ * wq8_stage2 followed by wq8_stage3. */
+wq8_status wq8_stage23(const wq8_plan *plan, const int8_t *Vq, const float *sV,
+                       const int8_t *Uq, const float *sU, void *y, void *stream);
 
 const char *wq8_status_string(wq8_status status);
 /* Detail of the last error on the calling host thread ("" if none). */

@@ -18,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libwino_q8_conv.so")
 
 WQ8_F32, WQ8_BF16 = 0, 1
+ALGOS = {"auto": 0, "staged": 1, "fused": 2}
 _DT = {torch.float32: WQ8_F32, torch.bfloat16: WQ8_BF16}
 
 
@@ -32,12 +33,13 @@ class wq8_desc(C.Structure):
                 ("s_B", C.POINTER(C.c_float)), ("s_G", C.POINTER(C.c_float)),
                 ("group", C.c_int), ("N", C.c_int), ("Cin", C.c_int), ("Cout", C.c_int),
                 ("H", C.c_int), ("W", C.c_int), ("pad", C.c_int),
-                ("x_dtype", C.c_int), ("y_dtype", C.c_int)]
+                ("x_dtype", C.c_int), ("y_dtype", C.c_int), ("algo", C.c_int)]
 
 
 EXPORTS = ("wq8_plan_create", "wq8_plan_destroy", "wq8_plan_query", "wq8_plan_matrices",
            "wq8_weights_prepare", "wq8_conv_forward", "wq8_stage1", "wq8_stage2",
-           "wq8_stage2_i32", "wq8_stage3", "wq8_status_string", "wq8_last_error")
+           "wq8_stage2_i32", "wq8_stage3", "wq8_stage23", "wq8_status_string",
+           "wq8_last_error")
 
 _lib = None
 
@@ -55,7 +57,8 @@ def load(path: str = LIB_PATH):
     lib.wq8_plan_create.argtypes = [C.POINTER(wq8_desc), C.POINTER(P)]
     lib.wq8_plan_destroy.argtypes = [P]
     lib.wq8_plan_destroy.restype = None
-    lib.wq8_plan_query.argtypes = [P, C.POINTER(S), C.POINTER(S), C.POINTER(S), C.POINTER(C.c_int64)]
+    lib.wq8_plan_query.argtypes = [P, C.POINTER(S), C.POINTER(S), C.POINTER(S), C.POINTER(C.c_int64),
+                                   C.POINTER(C.c_int)]
     lib.wq8_plan_matrices.argtypes = [P, P, P, P]
     lib.wq8_weights_prepare.argtypes = [P, P, P, P, P]
     lib.wq8_conv_forward.argtypes = [P, P, P, P, P, P, S, P]
@@ -63,6 +66,7 @@ def load(path: str = LIB_PATH):
     lib.wq8_stage2.argtypes = [P, P, P, P, P, P, P]
     lib.wq8_stage2_i32.argtypes = [P, P, P, P, P]
     lib.wq8_stage3.argtypes = [P, P, P, P, P, P]
+    lib.wq8_stage23.argtypes = [P, P, P, P, P, P, P]
     lib.wq8_status_string.argtypes = [i]
     lib.wq8_status_string.restype = C.c_char_p
     lib.wq8_last_error.argtypes = []
@@ -100,11 +104,11 @@ class Plan:
     """Owns a wq8_plan handle and the geometry needed to size buffers."""
 
     def __init__(self, m, N, Cin, Cout, H, W, pad=1, group=64, points=None, s_B=None, s_G=None,
-                 x_dtype=torch.float32, y_dtype=None):
+                 x_dtype=torch.float32, y_dtype=None, algo="auto"):
         lib = load()
         n = m + 2
         self.m, self.n, self.N, self.Cin, self.Cout, self.H, self.W = m, n, N, Cin, Cout, H, W
-        self.pad, self.group = pad, group
+        self.pad, self.group, self.algo = pad, group, algo
         self.x_dtype = x_dtype
         self.y_dtype = x_dtype if y_dtype is None else y_dtype
         self.Ho, self.Wo = H + 2 * pad - 2, W + 2 * pad - 2
@@ -121,16 +125,18 @@ class Plan:
 
         d = wq8_desc(m, arr(points, C.c_double, np.float64), arr(s_B, C.c_float, np.float32),
                      arr(s_G, C.c_float, np.float32), group, N, Cin, Cout, H, W, pad,
-                     _DT[self.x_dtype], _DT[self.y_dtype])
+                     _DT[self.x_dtype], _DT[self.y_dtype], ALGOS[algo])
         h = C.c_void_p()
         self._h = None
         _check(wq8_plan_create(d, h))
         self._h = h
-        ws, uc, us, t = C.c_size_t(), C.c_size_t(), C.c_size_t(), C.c_int64()
-        _check(lib.wq8_plan_query(h, C.byref(ws), C.byref(uc), C.byref(us), C.byref(t)))
+        ws, uc, us, t, al = C.c_size_t(), C.c_size_t(), C.c_size_t(), C.c_int64(), C.c_int()
+        _check(lib.wq8_plan_query(h, C.byref(ws), C.byref(uc), C.byref(us), C.byref(t),
+                                  C.byref(al)))
         self.workspace_bytes, self.u_code_bytes, self.u_scale_bytes = ws.value, uc.value, us.value
         self.T = t.value
         self.ng = Cin // group
+        self.fused = al.value == ALGOS["fused"]
 
     def __del__(self):
         if getattr(self, "_h", None) is not None and _lib is not None:
@@ -231,6 +237,14 @@ def wq8_stage3(plan: Plan, M, y=None, Yq=None, sY=None, want_codes=False, stream
         sY = torch.empty((plan.T, plan.Cout), dtype=torch.float32, device=M.device)
     _check(load().wq8_stage3(plan.handle, _ptr(M), _ptr(y), _ptr(Yq), _ptr(sY), _stream(stream)))
     return (y, Yq, sY) if want_codes else y
+
+
+def wq8_stage23(plan: Plan, Vq, sV, Uq, sU, y=None, stream=None):
+    if y is None:
+        y = plan.empty_output(Vq.device)
+    _check(load().wq8_stage23(plan.handle, _ptr(Vq), _ptr(sV), _ptr(Uq), _ptr(sU), _ptr(y),
+                              _stream(stream)))
+    return y
 
 
 def tiles(m, N, H, W, pad):

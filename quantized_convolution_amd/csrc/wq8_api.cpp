@@ -60,6 +60,7 @@ wq8_status wq8_conv_forward(const wq8_plan *p, const void *x, const int8_t *Uq, 
     float *sV = (float *)(ws + p->off_sv);
     float *M = (float *)(ws + p->off_m);
     WQ8_TRY(launch_stage1(p->geo, p->mats, p->xdt, x, Vq, sV, stream));
+    if (p->fused) return launch_fused23(p->geo, p->mats, p->ydt, Vq, sV, Uq, sU, y, stream);
     WQ8_TRY(launch_stage2(p->geo, Vq, sV, Uq, sU, M, nullptr, stream));
     return launch_stage3(p->geo, p->mats, p->ydt, M, y, nullptr, nullptr, stream);
 }
@@ -104,6 +105,18 @@ wq8_status wq8_stage3(const wq8_plan *p, const float *M, void *y, int8_t *Yq, fl
     if (Yq) WQ8_NEED(Yq);
     if (sY) WQ8_NEED(sY);
     return launch_stage3(p->geo, p->mats, p->ydt, M, y, Yq, sY, stream);
+}
+
+wq8_status wq8_stage23(const wq8_plan *p, const int8_t *Vq, const float *sV, const int8_t *Uq,
+                       const float *sU, void *y, void *stream) {
+    clear_error();
+    if (!p) return fail(WQ8_ERR_INVALID_ARG, "null plan");
+    WQ8_NEED(Vq);
+    WQ8_NEED(sV);
+    WQ8_NEED(Uq);
+    WQ8_NEED(sU);
+    WQ8_NEED(y);
+    return launch_fused23(p->geo, p->mats, p->ydt, Vq, sV, Uq, sU, y, stream);
 }
 
 }  // extern "C"

@@ -23,7 +23,17 @@ struct Geo {
     int N, Cin, Cout, H, W, pad;
     int Ho, Wo, tH, tW;
     int64_t T;                // tiles
+    int bt_std, at_std;       // 1 if B^T / A^T vanish wherever the standard
+                              // points' matrices do (zero terms may be skipped)
 };
+
+// Nonzero patterns of B^T [n][n] and A^T [m][n] for the standard points
+// 0, 1, -1, 2, -2, (1/2, -1/2,) infinity: bit (row * n + col) is set where the
+// entry is nonzero. Diagonal scales never change these patterns.
+constexpr uint64_t kBtPattern4 = 0xa9e79e795ull;
+constexpr uint64_t kBtPattern6 = 0xaa7e7e7e7e7e7e55ull;
+constexpr uint64_t kAtPattern4 = 0xf9e79full;
+constexpr uint64_t kAtPattern6 = 0xfe7e7e7e7e7full;
 
 // Set the thread-local error detail (printf-style) and return `st`.
 wq8_status fail(wq8_status st, const char *fmt, ...);
@@ -38,6 +48,9 @@ wq8_status launch_stage2(const Geo &g, const int8_t *Vq, const float *sV, const 
                          const float *sU, float *M, int32_t *P, void *stream);
 wq8_status launch_stage3(const Geo &g, const Mats &mt, wq8_dtype ydt, const float *M, void *y,
                          int8_t *Yq, float *sY, void *stream);
+wq8_status launch_fused23(const Geo &g, const Mats &mt, wq8_dtype ydt, const int8_t *Vq,
+                          const float *sV, const int8_t *Uq, const float *sU, void *y,
+                          void *stream);
 
 }  // namespace wq8
 
@@ -47,7 +60,8 @@ struct wq8_plan {
     wq8_dtype xdt, ydt;
     double points[wq8::kMaxN];
     float sB[wq8::kMaxN], sG[wq8::kMaxN];
-    // forward workspace layout (bytes)
+    int fused;  // stage 2 + 3 schedule chosen for the forward
+    // forward workspace layout (bytes); M is only used by the staged schedule
     size_t off_vq, off_sv, off_m, ws_bytes;
     size_t u_code_bytes, u_scale_bytes;
 };

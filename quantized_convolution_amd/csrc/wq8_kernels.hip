@@ -12,11 +12,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <type_traits>
+
 #include "wq8_internal.h"
 
 namespace wq8 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Raw buffer resources: one 128-bit scalar descriptor per array, so a load is
+// a lane offset (VGPR) plus a wave-uniform offset (SGPR) and no per-lane
+// 64-bit address has to be kept live. The plan keeps every array below 2^31
+// bytes, so 32-bit offsets cover them.
+constexpr int kBufferFlags = 0x00020000;  // gfx9 dword 3: 32-bit raw buffer
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, size_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, kBufferFlags);
+}
 
 // ----------------------------------------------------------------- helpers
 __device__ __forceinline__ float load_act(const float *p) { return *p; }
@@ -97,61 +109,258 @@ __device__ __forceinline__ void quantize_store(const float (&v)[NT], bool ok, in
     }
 }
 
-template <int M, int G, typename XT>
+// ------------------------------------------------------------- stage 1
+// One lane per input channel, one wave per (tile, 64-channel chunk); a block
+// of 4 waves walks tiles in a grid-stride loop. Per tile:
+//   1. load the n x n patch (rows skipped when outside the image; with
+//      W % 4 == 0, three aligned float4 loads per row and a uniform shift);
+//   2. V = B^T d B as fp32 fma chains in index order (terms whose B^T entry is
+//      structurally zero are skipped when the host has verified the pattern;
+//      fma(0, d, acc) == acc, so the chains stay bit-identical);
+//   3. group absmax per tap by a reduce-scatter butterfly over the group's
+//      lanes (permlane32/16 swaps, then DPP exchanges), leaving each lane the
+//      max of 64/SEG taps, so the IEEE divisions 127/a and a/127 run once per
+//      (tap, group) instead of once per value;
+//   4. reciprocals go through LDS to every lane of the group; each value is
+//      rounded with x + 1.5*2^23, whose low byte is rint(x) in two's
+//      complement (|x| <= 127 (1 + 2^-24)^2 < 127.5, so the clamp to +-127
+//      never binds and is omitted).
+constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
+
+// Reduce-scatter steps: pair a[i] with a[i + K/2]; each lane keeps one half
+// (the max over itself and its partner) and returns 1 if it kept the upper half.
+template <int K>
+__device__ __forceinline__ int rs_swap32(float (&a)[64]) {
+#pragma unroll
+    for (int i = 0; i < K / 2; ++i) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[i]), __float_as_uint(a[i + K / 2]),
+                                                  false, false);
+        a[i] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    auto lab = __builtin_amdgcn_permlane32_swap(0u, 1u, false, false);
+    return (int)lab[0];
+}
+
+template <int K>
+__device__ __forceinline__ int rs_swap16(float (&a)[64]) {
+#pragma unroll
+    for (int i = 0; i < K / 2; ++i) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(a[i + K / 2]),
+                                                  false, false);
+        a[i] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    auto lab = __builtin_amdgcn_permlane16_swap(0u, 1u, false, false);
+    return (int)lab[0];
+}
+
+// DPP exchange with the lane given by CTRL; BIT is a lane-id bit that differs
+// between partners and decides which half a lane keeps.
+template <int K, int CTRL, int BIT>
+__device__ __forceinline__ int rs_dpp(float (&a)[64], int lane) {
+    const bool up = (lane >> BIT) & 1;
+#pragma unroll
+    for (int i = 0; i < K / 2; ++i) {
+        const float lo = a[i], hi = a[i + K / 2];
+        const float send = up ? lo : hi, keep = up ? hi : lo;
+        const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xf, 0xf, false));
+        a[i] = fmaxf(keep, recv);
+    }
+    return up;
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppXor7 = 0x141;       // row_half_mirror: lane ^ 7 inside 8 lanes
+constexpr int kDppXor8 = 0x128;       // row_ror:8: lane ^ 8 inside 16 lanes
+
+// Max over SEG aligned lanes of 64 values per lane. On return a[j], j < 64/SEG,
+// holds the max for value index base + j (base is returned).
+template <int SEG>
+__device__ __forceinline__ int reduce_scatter_max(float (&a)[64], int lane) {
+    int base = 0;
+    if constexpr (SEG == 64) {
+        base += rs_swap32<64>(a) * 32;
+        base += rs_swap16<32>(a) * 16;
+        base += rs_dpp<16, kDppXor8, 3>(a, lane) * 8;
+        base += rs_dpp<8, kDppXor7, 2>(a, lane) * 4;
+        base += rs_dpp<4, kDppXor2, 1>(a, lane) * 2;
+        base += rs_dpp<2, kDppXor1, 0>(a, lane);
+    } else if constexpr (SEG == 32) {
+        base += rs_swap16<64>(a) * 32;
+        base += rs_dpp<32, kDppXor8, 3>(a, lane) * 16;
+        base += rs_dpp<16, kDppXor7, 2>(a, lane) * 8;
+        base += rs_dpp<8, kDppXor2, 1>(a, lane) * 4;
+        base += rs_dpp<4, kDppXor1, 0>(a, lane) * 2;
+    } else {
+        static_assert(SEG == 16, "group lanes must be 16, 32 or 64");
+        base += rs_dpp<64, kDppXor8, 3>(a, lane) * 32;
+        base += rs_dpp<32, kDppXor7, 2>(a, lane) * 16;
+        base += rs_dpp<16, kDppXor2, 1>(a, lane) * 8;
+        base += rs_dpp<8, kDppXor1, 0>(a, lane) * 4;
+    }
+    return base;
+}
+
+// n x n patch of one channel: rows outside the image and columns outside it
+// are zero.
+template <int N, bool VEC, typename XT>
+__device__ __forceinline__ void load_patch(const XT *__restrict__ xc, bool ok, int h0, int w0,
+                                           const Geo &g, float (&d)[N][N]) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const int h = h0 + k;
+        if (!ok || h < 0 || h >= g.H) {  // uniform except for ok (channel tail)
+#pragma unroll
+            for (int l = 0; l < N; ++l) d[k][l] = 0.0f;
+            continue;
+        }
+        const XT *row = xc + (size_t)h * g.W;
+        if constexpr (VEC) {
+            // W % 4 == 0: 4-float chunks never straddle a row end
+            const int wa = w0 >= 0 ? (w0 & ~3) : -4;
+            const int r = w0 - wa;  // 0..3, uniform
+            float win[12];
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int wc = wa + 4 * j;
+                float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (wc >= 0 && wc + 4 <= g.W) f = *(const float4 *)(row + wc);
+                win[4 * j] = f.x;
+                win[4 * j + 1] = f.y;
+                win[4 * j + 2] = f.z;
+                win[4 * j + 3] = f.w;
+            }
+            switch (r) {
+                case 0:
+#pragma unroll
+                    for (int l = 0; l < N; ++l) d[k][l] = win[l];
+                    break;
+                case 1:
+#pragma unroll
+                    for (int l = 0; l < N; ++l) d[k][l] = win[l + 1];
+                    break;
+                case 2:
+#pragma unroll
+                    for (int l = 0; l < N; ++l) d[k][l] = win[l + 2];
+                    break;
+                default:
+#pragma unroll
+                    for (int l = 0; l < N; ++l) d[k][l] = win[l + 3];
+                    break;
+            }
+        } else {
+#pragma unroll
+            for (int l = 0; l < N; ++l) {
+                const int w = w0 + l;
+                d[k][l] = (w >= 0 && w < g.W) ? load_act(row + w) : 0.0f;
+            }
+        }
+    }
+}
+
+template <int M, int G, uint64_t BMASK, bool VEC, typename XT>
 __global__ __launch_bounds__(256) void k_stage1(const XT *__restrict__ x, int8_t *__restrict__ Vq,
                                                 float *__restrict__ sV, Mats mt, Geo g) {
     constexpr int N = M + 2, NT = N * N;
     using S = GroupShape<G>;
-    __shared__ float red[S::GW > 1 ? 4 : 1][NT];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * S::TPB + wave / S::GW;
+    constexpr int KF = 64 / S::SEG;  // taps per lane after the reduce-scatter
+    __shared__ float red[S::GW > 1 ? 4 : 1][64];
+    __shared__ __attribute__((aligned(16))) float inv_lds[4][64 / S::SEG][64];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int c = blockIdx.y * S::CPB + (wave % S::GW) * 64 + lane;
-    const bool ok = t < g.T && c < g.Cin;
+    const bool cok = c < g.Cin;
+    const int seg = lane / S::SEG;
+    const size_t plane = (size_t)g.T * g.Cin, splane = (size_t)g.T * g.ng;
+    const int ntb = (int)((g.T + S::TPB - 1) / S::TPB);
 
-    float v[NT];
-    {
+    for (int tb = blockIdx.x; tb < ntb; tb += gridDim.x) {
+        const int t = tb * S::TPB + wave / S::GW;  // uniform per wave
+        const bool tok = t < g.T;
+        const bool ok = tok && cok;
         int img = 0, ty = 0, tx = 0;
-        if (ok) {
+        if (tok) {
             tx = t % g.tW;
             const int r = t / g.tW;
             ty = r % g.tH;
             img = r / g.tH;
         }
-        const int h0 = ty * M - g.pad, w0 = tx * M - g.pad;
-        const XT *xc = x + ((size_t)img * g.Cin + (ok ? c : 0)) * g.H * g.W;
-        float d[N][N];
+        float v[NT];
+        {
+            float d[N][N];
+            const XT *xc = x + ((size_t)img * g.Cin + (cok ? c : 0)) * g.H * g.W;
+            load_patch<N, VEC, XT>(xc, ok, ty * M - g.pad, tx * M - g.pad, g, d);
+            float t1[N][N];
 #pragma unroll
-        for (int k = 0; k < N; ++k)
+            for (int i = 0; i < N; ++i)
 #pragma unroll
-            for (int l = 0; l < N; ++l) {
-                const int h = h0 + k, w = w0 + l;
-                d[k][l] = (ok && h >= 0 && h < g.H && w >= 0 && w < g.W)
-                              ? load_act(xc + (size_t)h * g.W + w)
-                              : 0.0f;
+                for (int l = 0; l < N; ++l) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < N; ++k)
+                        if ((BMASK >> (i * N + k)) & 1) acc = __builtin_fmaf(mt.Bt[i * N + k], d[k][l], acc);
+                    t1[i][l] = acc;
+                }
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+#pragma unroll
+                for (int j = 0; j < N; ++j) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int l = 0; l < N; ++l)
+                        if ((BMASK >> (j * N + l)) & 1) acc = __builtin_fmaf(t1[i][l], mt.Bt[j * N + l], acc);
+                    v[i * N + j] = acc;
+                }
+        }
+        float a[64];
+#pragma unroll
+        for (int i = 0; i < 64; ++i) a[i] = i < NT ? fabsf(v[i]) : 0.0f;
+        const int base = reduce_scatter_max<S::SEG>(a, lane);
+        if constexpr (S::GW > 1) {
+#pragma unroll
+            for (int j = 0; j < KF; ++j) red[wave][base + j] = a[j];
+            __syncthreads();
+            const int w0 = (wave / S::GW) * S::GW;
+#pragma unroll
+            for (int j = 0; j < KF; ++j) {
+                float m = red[w0][base + j];
+#pragma unroll
+                for (int k = 1; k < S::GW; ++k) m = fmaxf(m, red[w0 + k][base + j]);
+                a[j] = m;
             }
-        float t1[N][N];
+        }
 #pragma unroll
-        for (int i = 0; i < N; ++i)
-#pragma unroll
-            for (int l = 0; l < N; ++l) {
-                float acc = 0.0f;
-#pragma unroll
-                for (int k = 0; k < N; ++k) acc = __builtin_fmaf(mt.Bt[i * N + k], d[k][l], acc);
-                t1[i][l] = acc;
+        for (int j = 0; j < KF; ++j) {
+            const int tap = base + j;
+            const float am = a[j];
+            float inv = 0.0f, sc = 0.0f;
+            if (am != 0.0f) {
+                inv = 127.0f / am;
+                sc = am / 127.0f;
             }
+            inv_lds[wave][seg][tap] = inv;
+            if (ok && tap < NT && (S::GW == 1 || wave % S::GW == 0))
+                sV[tap * splane + (size_t)t * g.ng + c / G] = sc;
+        }
+        __syncthreads();
+        if (ok) {
+            int8_t *vp = Vq + (size_t)t * g.Cin + c;
 #pragma unroll
-        for (int i = 0; i < N; ++i)
+            for (int q4 = 0; q4 < (NT + 3) / 4; ++q4) {
+                const float4 iv = *(const float4 *)&inv_lds[wave][seg][4 * q4];
+                const float ivs[4] = {iv.x, iv.y, iv.z, iv.w};
 #pragma unroll
-            for (int j = 0; j < N; ++j) {
-                float acc = 0.0f;
-#pragma unroll
-                for (int l = 0; l < N; ++l) acc = __builtin_fmaf(t1[i][l], mt.Bt[j * N + l], acc);
-                v[i * N + j] = acc;
+                for (int e = 0; e < 4; ++e) {
+                    const int tap = 4 * q4 + e;
+                    if (tap < NT) {
+                        const float y = v[tap] * ivs[e] + kRoundMagic;
+                        vp[tap * plane] = (int8_t)__float_as_uint(y);
+                    }
+                }
             }
+        }
+        __syncthreads();  // inv_lds is rewritten by the next tile
     }
-    const size_t plane = (size_t)g.T * g.Cin, splane = (size_t)g.T * g.ng;
-    quantize_store<NT, G>(v, ok, c, wave, Vq + (size_t)t * g.Cin + c, plane,
-                          sV + (size_t)t * g.ng + c / G, splane, red);
 }
 
 template <int M, int G>
@@ -237,6 +446,7 @@ __global__ __launch_bounds__(256) void k_stage2(const int8_t *__restrict__ Vq,
         for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
             for (int bj = 0; bj < 2; ++bj) p[bi][bj] = v4i{0, 0, 0, 0};
+        // rows past T / Cout read row 0; their products are never stored
         if constexpr (KS == 64) {
             // G is a multiple of 64: G / 64 MFMA K-steps per group
             for (int k0 = gi * g.G; k0 < (gi + 1) * g.G; k0 += 64) {
@@ -244,14 +454,12 @@ __global__ __launch_bounds__(256) void k_stage2(const int8_t *__restrict__ Vq,
 #pragma unroll
                 for (int bi = 0; bi < 2; ++bi) {
                     const int row = tb + 16 * bi + r;
-                    a[bi] = row < g.T ? *(const v4i *)(Vp + (size_t)row * g.Cin + k0 + 16 * kq)
-                                      : v4i{0, 0, 0, 0};
+                    a[bi] = *(const v4i *)(Vp + (size_t)(row < g.T ? row : 0) * g.Cin + k0 + 16 * kq);
                 }
 #pragma unroll
                 for (int bj = 0; bj < 2; ++bj) {
                     const int col = cb + 16 * bj + r;
-                    b[bj] = col < g.Cout ? *(const v4i *)(Up + (size_t)col * g.Cin + k0 + 16 * kq)
-                                         : v4i{0, 0, 0, 0};
+                    b[bj] = *(const v4i *)(Up + (size_t)(col < g.Cout ? col : 0) * g.Cin + k0 + 16 * kq);
                 }
 #pragma unroll
                 for (int bi = 0; bi < 2; ++bi)
@@ -261,18 +469,20 @@ __global__ __launch_bounds__(256) void k_stage2(const int8_t *__restrict__ Vq,
             }
         } else {
             // G = 16 or 32: one K = 32 step per group; K slots past the group are zero
-            const int k0 = gi * g.G;
             const bool kin = 8 * kq < g.G;
+            const int k0 = gi * g.G + (kin ? 8 * kq : 0);
             long a[2], b[2];
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi) {
                 const int row = tb + 16 * bi + r;
-                a[bi] = (kin && row < g.T) ? *(const long *)(Vp + (size_t)row * g.Cin + k0 + 8 * kq) : 0;
+                const long v = *(const long *)(Vp + (size_t)(row < g.T ? row : 0) * g.Cin + k0);
+                a[bi] = kin ? v : 0;
             }
 #pragma unroll
             for (int bj = 0; bj < 2; ++bj) {
                 const int col = cb + 16 * bj + r;
-                b[bj] = (kin && col < g.Cout) ? *(const long *)(Up + (size_t)col * g.Cin + k0 + 8 * kq) : 0;
+                const long v = *(const long *)(Up + (size_t)(col < g.Cout ? col : 0) * g.Cin + k0);
+                b[bj] = kin ? v : 0;
             }
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi)
@@ -372,6 +582,208 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
         }
 }
 
+// ------------------------------------------------- fused stages 2 + 3
+// The Winograd-domain output M never leaves the chip. A block owns 16 tiles x
+// 16 output channels and all n*n taps; wave w computes taps
+// [w*NT/4, (w+1)*NT/4) of that 16 x 16 block on MFMA with U as the A operand
+// (rows = output channels) and V as the B operand (columns = tiles), so lane
+// (r, kq) ends with the four (co = 4kq + i, t = r) pairs for its taps. The
+// per-group dequantization is the same fma chain over groups as stage 2. The
+// Y absmax over all taps of a pair combines the four waves' partial maxima
+// through LDS; the rounded codes go to LDS, and in the epilogue each lane
+// takes one (tile, co) pair and applies A^T Yq A (fp32 fma chains in index
+// order, structurally zero A^T terms skipped) and the scale.
+template <int M, int G, uint64_t AMASK, typename YT>
+__global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
+                                                 const float *__restrict__ sV,
+                                                 const int8_t *__restrict__ Uq,
+                                                 const float *__restrict__ sU, YT *__restrict__ y,
+                                                 Mats mt, Geo g) {
+    constexpr int N = M + 2, NT = N * N, TPW = NT / 4;
+    constexpr bool K64 = G % 64 == 0;
+    constexpr int KSTEPS = K64 ? G / 64 : 1;
+    constexpr int PST = NT + 4;  // padded pair stride in LDS (floats)
+    __shared__ __attribute__((aligned(16))) float codes[256 * PST];
+    __shared__ float pmax[4][256];
+    __shared__ float sy_lds[256];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    const int nco = (g.Cout + 15) / 16;
+    const int cob = blockIdx.x % nco, tb = blockIdx.x / nco;
+    const int t0 = tb * 16, co0 = cob * 16;
+    const int tap0 = wave * TPW;
+    const size_t vplane = (size_t)g.T * g.Cin, uplane = (size_t)g.Cout * g.Cin;
+
+    // ---- Hadamard GEMMs for this wave's taps
+    // Rows past T or Cout read row 0 instead: they only feed (tile, co) pairs
+    // that are never stored, and unconditional loads let the compiler keep
+    // many taps' operands in flight.
+    const int tB = t0 + r;          // B column: tile
+    const int coA = co0 + r;        // A row: output channel
+    const int tBc = tB < g.T ? tB : 0, coAc = coA < g.Cout ? coA : 0;
+    const int n2 = g.n * g.n;
+    const auto rV = make_rsrc(Vq, (size_t)n2 * vplane);
+    const auto rU = make_rsrc(Uq, (size_t)n2 * uplane);
+    const auto rsV = make_rsrc(sV, (size_t)n2 * g.T * g.ng * 4);
+    const auto rsU = make_rsrc(sU, (size_t)n2 * g.Cout * g.ng * 4);
+    // lane offsets (bytes) that do not change with the tap or group
+    const bool kin = K64 || 8 * kq < G;          // K slots inside the group
+    const int koff = K64 ? 16 * kq : (kin ? 8 * kq : 0);
+    const int voff = tBc * g.Cin + koff;
+    const int uoff = coAc * g.Cin + koff;
+    const int svoff = tBc * g.ng * 4;
+    int suoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int co = co0 + 4 * kq + i;
+        suoff[i] = (co < g.Cout ? co : 0) * g.ng * 4;
+    }
+    float acc[TPW][4];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] = 0.0f;
+
+    // Operands of one tap for one group.
+    struct TapOps {
+        v4i a[K64 ? KSTEPS : 1], b[K64 ? KSTEPS : 1];
+        float sv, su[4];
+    };
+    auto load_tap = [&](int j, int gi, TapOps &o) {
+        const int tap = tap0 + j;
+        const int vs = tap * (int)vplane + gi * G, us = tap * (int)uplane + gi * G;
+        if constexpr (K64) {
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                o.a[ks] = __builtin_amdgcn_raw_buffer_load_b128(rU, uoff, us + ks * 64, 0);
+                o.b[ks] = __builtin_amdgcn_raw_buffer_load_b128(rV, voff, vs + ks * 64, 0);
+            }
+        } else {
+            const auto a2 = __builtin_amdgcn_raw_buffer_load_b64(rU, uoff, us, 0);
+            const auto b2 = __builtin_amdgcn_raw_buffer_load_b64(rV, voff, vs, 0);
+            o.a[0] = v4i{(int)a2[0], (int)a2[1], 0, 0};
+            o.b[0] = v4i{(int)b2[0], (int)b2[1], 0, 0};
+        }
+        o.sv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsV, svoff,
+                                                                    (tap * (int)g.T * g.ng + gi) * 4, 0));
+        const int su_s = (tap * g.Cout * g.ng + gi) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o.su[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsU, suoff[i], su_s, 0));
+    };
+    auto use_tap = [&](int j, const TapOps &o) {
+        v4i P = v4i{0, 0, 0, 0};
+        if constexpr (K64) {
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+                P = __builtin_amdgcn_mfma_i32_16x16x64_i8(o.a[ks], o.b[ks], P, 0, 0, 0);
+        } else {
+            // K = 32; for G = 16 the upper 16 K slots are zero
+            long a = ((long)(uint32_t)o.a[0][1] << 32) | (uint32_t)o.a[0][0];
+            long b = ((long)(uint32_t)o.b[0][1] << 32) | (uint32_t)o.b[0][0];
+            a = kin ? a : 0;
+            b = kin ? b : 0;
+            P = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, P, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float sc = o.sv * o.su[i];
+            acc[j][i] = __builtin_fmaf(sc, (float)P[i], acc[j][i]);
+        }
+    };
+    // two batches of taps in flight: the next batch's loads are issued before
+    // the current batch's MFMAs and dequantization
+    constexpr int BATCH = KSTEPS >= 4 ? 1 : KSTEPS == 2 ? (TPW % 2 == 0 ? 2 : 3)
+                                                        : (TPW % 4 == 0 ? 4 : 3);
+    for (int gi = 0; gi < g.ng; ++gi) {
+        TapOps buf[2][BATCH];
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) load_tap(b, gi, buf[0][b]);
+#pragma unroll
+        for (int jb = 0; jb < TPW; jb += BATCH) {
+            const int cur = (jb / BATCH) & 1;
+            if (jb + BATCH < TPW)
+#pragma unroll
+                for (int b = 0; b < BATCH; ++b) load_tap(jb + BATCH + b, gi, buf[cur ^ 1][b]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) use_tap(jb + b, buf[cur][b]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // ---- Y: one scale per (tile, co) over all taps
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) m = fmaxf(m, fabsf(acc[j][i]));
+        pmax[wave][(4 * kq + i) * 16 + r] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = (4 * kq + i) * 16 + r;
+        const float am = fmaxf(fmaxf(pmax[0][p], pmax[1][p]), fmaxf(pmax[2][p], pmax[3][p]));
+        float inv = 0.0f, sy = 0.0f;
+        if (am != 0.0f) {
+            inv = 127.0f / am;
+            sy = am / 127.0f;
+        }
+        if (wave == 0) sy_lds[p] = sy;
+        float *cp = codes + p * PST + tap0;
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) cp[j] = __builtin_rintf(acc[j][i] * inv);
+    }
+    __syncthreads();
+
+    // ---- output transform, one (tile, co) pair per lane
+    const int p = wave * 64 + lane;
+    const int tl = p & 15, col = p >> 4;
+    const int t = t0 + tl, co = co0 + col;
+    if (t >= g.T || co >= g.Cout) return;
+    float q[NT];
+    const float *cp = codes + p * PST;
+#pragma unroll
+    for (int k = 0; k < NT / 4; ++k) {
+        const float4 f = *(const float4 *)(cp + 4 * k);
+        q[4 * k] = f.x;
+        q[4 * k + 1] = f.y;
+        q[4 * k + 2] = f.z;
+        q[4 * k + 3] = f.w;
+    }
+    const float sy = sy_lds[p];
+    float z[M][N];
+#pragma unroll
+    for (int a = 0; a < M; ++a)
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            float acc2 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                if ((AMASK >> (a * N + i)) & 1) acc2 = __builtin_fmaf(mt.At[a * N + i], q[i * N + j], acc2);
+            z[a][j] = acc2;
+        }
+    const int tx = t % g.tW, rr = t / g.tW, ty = rr % g.tH, img = rr / g.tH;
+    YT *yp = y + ((size_t)img * g.Cout + co) * g.Ho * g.Wo;
+#pragma unroll
+    for (int a = 0; a < M; ++a) {
+        const int h = ty * M + a;
+        if (h >= g.Ho) break;
+#pragma unroll
+        for (int b = 0; b < M; ++b) {
+            float o = 0.0f;
+#pragma unroll
+            for (int j = 0; j < N; ++j)
+                if ((AMASK >> (b * N + j)) & 1) o = __builtin_fmaf(z[a][j], mt.At[b * N + j], o);
+            const int w = tx * M + b;
+            if (w < g.Wo) store_act(yp + (size_t)h * g.Wo + w, o * sy);
+        }
+    }
+}
+
 // ------------------------------------------------------------- launchers
 static wq8_status check_launch(const char *what) {
     hipError_t e = hipGetLastError();
@@ -407,12 +819,31 @@ wq8_status launch_weights(const Geo &g, const Mats &mt, const float *w, int8_t *
     return check_launch("weight transform");
 }
 
+template <int M, int G, uint64_t BMASK, bool VEC, typename XT>
+static void stage1_launch(const Geo &g, const Mats &mt, const XT *x, int8_t *Vq, float *sV,
+                          hipStream_t s) {
+    using S = GroupShape<G>;
+    const int ntb = (int)((g.T + S::TPB - 1) / S::TPB);
+    const int cblocks = (g.Cin + S::CPB - 1) / S::CPB;
+    // enough blocks for 8 per CU over the 256 CUs, each looping over tiles
+    const int bx = std::max(1, std::min(ntb, (2048 + cblocks - 1) / cblocks));
+    hipLaunchKernelGGL((k_stage1<M, G, BMASK, VEC, XT>), dim3(bx, cblocks), dim3(256), 0, s, x, Vq,
+                       sV, mt, g);
+}
+
 template <int M, int G, typename XT>
 static void stage1_m_g(const Geo &g, const Mats &mt, const XT *x, int8_t *Vq, float *sV,
                        hipStream_t s) {
-    using S = GroupShape<G>;
-    dim3 grid((unsigned)((g.T + S::TPB - 1) / S::TPB), (g.Cin + S::CPB - 1) / S::CPB);
-    hipLaunchKernelGGL((k_stage1<M, G, XT>), grid, dim3(256), 0, s, x, Vq, sV, mt, g);
+    constexpr uint64_t pat = M == 4 ? kBtPattern4 : kBtPattern6;
+    constexpr bool can_vec = std::is_same<XT, float>::value;
+    const bool vec = can_vec && g.W % 4 == 0;
+    if (g.bt_std) {
+        if (vec) stage1_launch<M, G, pat, can_vec, XT>(g, mt, x, Vq, sV, s);
+        else stage1_launch<M, G, pat, false, XT>(g, mt, x, Vq, sV, s);
+    } else {
+        if (vec) stage1_launch<M, G, ~0ull, can_vec, XT>(g, mt, x, Vq, sV, s);
+        else stage1_launch<M, G, ~0ull, false, XT>(g, mt, x, Vq, sV, s);
+    }
 }
 
 template <int M, typename XT>
@@ -462,6 +893,45 @@ static void stage3_m(const Geo &g, const Mats &mt, const float *Mi, YT *y, int8_
     const int64_t work = (int64_t)g.T * g.Cout;
     dim3 grid((unsigned)((work + 255) / 256));
     hipLaunchKernelGGL((k_stage3<M, YT>), grid, dim3(256), 0, s, Mi, y, Yq, sY, mt, g);
+}
+
+template <int M, int G, typename YT>
+static void fused_m_g(const Geo &g, const Mats &mt, const int8_t *Vq, const float *sV,
+                      const int8_t *Uq, const float *sU, YT *y, hipStream_t s) {
+    constexpr uint64_t pat = M == 4 ? kAtPattern4 : kAtPattern6;
+    const unsigned blocks = (unsigned)(((g.T + 15) / 16) * ((g.Cout + 15) / 16));
+    if (g.at_std)
+        hipLaunchKernelGGL((k_fused23<M, G, pat, YT>), dim3(blocks), dim3(256), 0, s, Vq, sV, Uq, sU, y,
+                           mt, g);
+    else
+        hipLaunchKernelGGL((k_fused23<M, G, ~0ull, YT>), dim3(blocks), dim3(256), 0, s, Vq, sV, Uq, sU,
+                           y, mt, g);
+}
+
+template <int M, typename YT>
+static void fused_m(const Geo &g, const Mats &mt, const int8_t *Vq, const float *sV,
+                    const int8_t *Uq, const float *sU, YT *y, hipStream_t s) {
+    switch (g.G) {
+        case 16: fused_m_g<M, 16>(g, mt, Vq, sV, Uq, sU, y, s); break;
+        case 32: fused_m_g<M, 32>(g, mt, Vq, sV, Uq, sU, y, s); break;
+        case 64: fused_m_g<M, 64>(g, mt, Vq, sV, Uq, sU, y, s); break;
+        case 128: fused_m_g<M, 128>(g, mt, Vq, sV, Uq, sU, y, s); break;
+        default: fused_m_g<M, 256>(g, mt, Vq, sV, Uq, sU, y, s); break;
+    }
+}
+
+wq8_status launch_fused23(const Geo &g, const Mats &mt, wq8_dtype ydt, const int8_t *Vq,
+                          const float *sV, const int8_t *Uq, const float *sU, void *y,
+                          void *stream) {
+    hipStream_t s = (hipStream_t)stream;
+    if (ydt == WQ8_F32) {
+        if (g.m == 4) fused_m<4>(g, mt, Vq, sV, Uq, sU, (float *)y, s);
+        else fused_m<6>(g, mt, Vq, sV, Uq, sU, (float *)y, s);
+    } else {
+        if (g.m == 4) fused_m<4>(g, mt, Vq, sV, Uq, sU, (uint16_t *)y, s);
+        else fused_m<6>(g, mt, Vq, sV, Uq, sU, (uint16_t *)y, s);
+    }
+    return check_launch("fused Hadamard + output transform");
 }
 
 wq8_status launch_stage3(const Geo &g, const Mats &mt, wq8_dtype ydt, const float *Mi, void *y,

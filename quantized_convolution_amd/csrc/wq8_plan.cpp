@@ -325,7 +325,9 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
     // per-tap planes with 32-bit element counts inside a kernel
     const int64_t n2 = (int64_t)n * n;
     const int64_t lim = (int64_t)1 << 31;
-    if (g.T * d->Cin >= lim || g.T * d->Cout >= lim || (int64_t)d->Cout * d->Cin >= lim ||
+    // the kernels address Vq, sV, Uq, sU and M with 32-bit byte offsets
+    if (n2 * g.T * d->Cin >= lim || n2 * g.T * d->Cout * 4 >= lim ||
+        n2 * (int64_t)d->Cout * d->Cin >= lim ||
         (int64_t)d->N * d->Cin * d->H * d->W >= lim * 4 ||
         (int64_t)d->N * d->Cout * g.Ho * g.Wo >= lim * 4)
         return fail(WQ8_ERR_UNSUPPORTED, "problem too large for this build");
@@ -386,13 +388,37 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
     for (int i = 0; i < n * 3; ++i)
         if (!isfinite(mt.G[i])) return fail(WQ8_ERR_INVALID_ARG, "G overflows fp32");
 
+    // may the kernels skip the structurally zero terms of the standard points?
+    {
+        uint64_t bt_nz = 0, at_nz = 0;
+        for (int i = 0; i < n * n; ++i)
+            if (mt.Bt[i] != 0.0f) bt_nz |= 1ull << i;
+        for (int i = 0; i < m * n; ++i)
+            if (mt.At[i] != 0.0f) at_nz |= 1ull << i;
+        const uint64_t bt_pat = m == 4 ? kBtPattern4 : kBtPattern6;
+        const uint64_t at_pat = m == 4 ? kAtPattern4 : kAtPattern6;
+        g.bt_std = (bt_nz & ~bt_pat) == 0;
+        g.at_std = (at_nz & ~at_pat) == 0;
+    }
+
     // workspace: Vq | sV | M, each 256-byte aligned
     p->off_vq = 0;
     p->off_sv = round_up((size_t)(n2 * g.T * g.Cin), 256);
     p->off_m = p->off_sv + round_up((size_t)(n2 * g.T * g.ng) * 4, 256);
-    p->ws_bytes = p->off_m + (size_t)(n2 * g.T * g.Cout) * 4;
     p->u_code_bytes = (size_t)(n2 * g.Cout * g.Cin);
     p->u_scale_bytes = (size_t)(n2 * g.Cout * g.ng) * 4;
+    if (d->algo != WQ8_ALGO_AUTO && d->algo != WQ8_ALGO_STAGED && d->algo != WQ8_ALGO_FUSED)
+        return fail(WQ8_ERR_INVALID_ARG, "unknown algo %d", (int)d->algo);
+    if (d->algo == WQ8_ALGO_AUTO) {
+        // the fused kernel re-reads the weights once per 16-tile block (from
+        // L2 / Infinity Cache when they fit); the staged one writes and reads M
+        const double reread = (double)p->u_code_bytes * (double)((g.T + 15) / 16);
+        const double mbytes = 8.0 * (double)(n2 * g.T * g.Cout);
+        p->fused = p->u_code_bytes <= ((size_t)4 << 20) || reread <= mbytes;
+    } else {
+        p->fused = d->algo == WQ8_ALGO_FUSED;
+    }
+    p->ws_bytes = p->fused ? p->off_m : p->off_m + (size_t)(n2 * g.T * g.Cout) * 4;
     return WQ8_OK;
 }
 
@@ -419,13 +445,14 @@ wq8_status wq8_plan_create(const wq8_desc *desc, wq8_plan **out) {
 void wq8_plan_destroy(wq8_plan *plan) { delete plan; }
 
 wq8_status wq8_plan_query(const wq8_plan *p, size_t *ws, size_t *ucode, size_t *uscale,
-                          int64_t *tiles) {
+                          int64_t *tiles, wq8_algo *algo) {
     wq8::clear_error();
     if (!p) return wq8::fail(WQ8_ERR_INVALID_ARG, "null plan");
     if (ws) *ws = p->ws_bytes;
     if (ucode) *ucode = p->u_code_bytes;
     if (uscale) *uscale = p->u_scale_bytes;
     if (tiles) *tiles = p->geo.T;
+    if (algo) *algo = p->fused ? WQ8_ALGO_FUSED : WQ8_ALGO_STAGED;
     return WQ8_OK;
 }
 

@@ -57,9 +57,9 @@ def assert_out(got, ref, what):
     return err
 
 
-def make_plan(L, d, xdt=torch.float32, ydt=None):
+def make_plan(L, d, xdt=torch.float32, ydt=None, algo="auto"):
     return q.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"], s_B=d["s_b"],
-                  s_G=d["s_g"], x_dtype=xdt, y_dtype=ydt)
+                  s_G=d["s_g"], x_dtype=xdt, y_dtype=ydt, algo=algo)
 
 
 def to_dev(a, dev):
@@ -120,11 +120,18 @@ def test_stages_and_forward(dev, L):
     assert_codes(Yq.cpu().numpy(), ref["Yq"], "Yq")
     assert np.array_equal(sY.cpu().numpy(), ref["sY"])
     assert_out(y3.cpu().numpy(), ref["y"], "stage-3 output")
-    # whole forward
-    y = q.wq8_conv_forward(plan, to_dev(d["x"], dev), Uq, sU)
+    # fused stages 2 + 3 from the oracle's codes
+    y23 = q.wq8_stage23(plan, oVq, to_dev(ref["sV"], dev), oUq, to_dev(ref["sU"], dev))
     torch.cuda.synchronize()
-    err = assert_out(y.cpu().numpy(), ref["y"], "forward")
-    print(f"[case] {L.name}: forward max err {err:.3e} (rms {rms(ref['y']):.3e})", flush=True)
+    assert_out(y23.cpu().numpy(), ref["y"], "fused stage-2+3 output")
+    # whole forward, both schedules
+    for algo in ("staged", "fused"):
+        p2 = make_plan(L, d, algo=algo)
+        y = q.wq8_conv_forward(p2, to_dev(d["x"], dev), Uq, sU)
+        torch.cuda.synchronize()
+        err = assert_out(y.cpu().numpy(), ref["y"], f"forward ({algo})")
+        print(f"[case] {L.name}: {algo} forward max err {err:.3e} (rms {rms(ref['y']):.3e})",
+              flush=True)
 
 
 @pytest.mark.parametrize("xdt,ydt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.bfloat16),
@@ -179,19 +186,20 @@ def test_forward_is_deterministic(dev):
 FULL = list(WL.LAYERS.values())
 
 
+@pytest.mark.parametrize("algo", ["staged", "fused"])
 @pytest.mark.parametrize("L", FULL, ids=ids(FULL))
-def test_full_size_sampled(dev, L):
+def test_full_size_sampled(dev, L, algo):
     """Full configuration, launched exactly as the benchmark launches it
     (wq8_conv_forward with a plan-sized workspace). Transforms and codes are
     compared in full; the Hadamard stage, Y codes and outputs at 192 sampled
     (tile, co) pairs that the oracle evaluates one by one."""
-    print(f"\n[case] full {L.name}", flush=True)
+    print(f"\n[case] full {L.name} ({algo})", flush=True)
     d = WL.make(L)
     from oracle import transforms as T
     Bt, Gm, At = T.transforms_f32(L.m, list(d["points"]), d["s_b"], d["s_g"])
     oUq, osU = oracle.weights(L.m, d["w"], L.G, Gm)
     oVq, osV = oracle.stage1(L.m, d["x"], L.pad, L.G, Bt)
-    plan = make_plan(L, d)
+    plan = make_plan(L, d, algo=algo)
     x = to_dev(d["x"], dev)
     Uq, sU = q.wq8_weights_prepare(plan, to_dev(d["w"], dev))
     y = q.wq8_conv_forward(plan, x, Uq, sU, workspace=plan.empty_workspace(dev))
@@ -223,4 +231,4 @@ def test_full_size_sampled(dev, L):
     # RMS of the whole oracle output is estimated from the sampled tiles
     err = float(np.max(np.abs(got.astype(np.float64) - want)))
     assert err <= OUT_TOL * rms(want), f"max err {err:.3e} rms {rms(want):.3e}"
-    print(f"[case] full {L.name}: sampled max err {err:.3e}", flush=True)
+    print(f"[case] full {L.name} ({algo}): sampled max err {err:.3e}", flush=True)

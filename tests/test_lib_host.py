@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def _create(**kw):
     base = dict(m=6, points=None, s_B=None, s_G=None, group=64, N=1, Cin=64, Cout=64, H=16, W=16,
-                pad=1, x_dtype=0, y_dtype=0)
+                pad=1, x_dtype=0, y_dtype=0, algo=0)
     base.update(kw)
     keep = []
 
@@ -53,7 +53,7 @@ def _create(**kw):
     d = B.wq8_desc(base["m"], arr(base["points"], C.c_double, np.float64),
                    arr(base["s_B"], C.c_float, np.float32), arr(base["s_G"], C.c_float, np.float32),
                    base["group"], base["N"], base["Cin"], base["Cout"], base["H"], base["W"],
-                   base["pad"], base["x_dtype"], base["y_dtype"])
+                   base["pad"], base["x_dtype"], base["y_dtype"], base["algo"])
     h = C.c_void_p()
     st = B.wq8_plan_create(d, h)
     if st == 0:
@@ -70,7 +70,7 @@ def _create(**kw):
     (dict(pad=3), -1), (dict(pad=-1), -1),
     (dict(H=1, W=1, pad=0), -1), (dict(H=1, W=1, pad=1), 0),
     (dict(N=0), -1), (dict(Cout=0), -1),
-    (dict(x_dtype=7), -1),
+    (dict(x_dtype=7), -1), (dict(algo=3), -1), (dict(algo=1), 0), (dict(algo=2), 0),
     (dict(points=[0, 1, -1, 2, 2, .5, -.5, math.inf]), -3),
     (dict(points=[0, 1, -1, 2, -2, .5, math.inf, math.inf]), -3),
     (dict(points=[0, 1, -1, 2, -2, .5, -.5, math.nan]), -1),
@@ -117,7 +117,7 @@ def test_plan_matrices_equal_exactly_rounded(m):
 
 def test_plan_query_sizes():
     L = WL.LAYERS[WL.BENCH_LAYER]
-    plan = B.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G)
+    plan = B.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, algo="staged")
     n2 = L.n ** 2
     assert plan.T == L.tiles == 3200
     assert plan.u_code_bytes == n2 * L.Cout * L.Cin
@@ -128,7 +128,7 @@ def test_plan_query_sizes():
 @pytest.mark.skipif(HAS_GPU, reason="host-only argument checks; uses fake device pointers")
 def test_forward_rejects_bad_arguments_before_launch():
     lib = B.load()
-    plan = B.Plan(6, 1, 64, 64, 16, 16, 1, 64)
+    plan = B.Plan(6, 1, 64, 64, 16, 16, 1, 64, algo="staged")
     h = plan.handle
     good = C.c_void_p(0x10000)
     ws = plan.workspace_bytes
@@ -140,3 +140,13 @@ def test_forward_rejects_bad_arguments_before_launch():
     assert f(h, good, good, good, good, C.c_void_p(0x30000), ws, None) == -1   # x == y
     assert lib.wq8_stage3(h, good, None, None, None, None) == -1
     assert lib.wq8_stage3(h, good, good, C.c_void_p(0x40008), None, None) == -5
+
+
+def test_plan_reports_schedule():
+    small = B.Plan(6, 32, 64, 64, 56, 56, 1, 64)                 # 256 KB of weights: fused
+    big = B.Plan(6, 8, 1280, 1280, 16, 16, 1, 32)                # 105 MB of weights: staged
+    assert small.fused and not big.fused
+    assert B.Plan(6, 8, 1280, 1280, 16, 16, 1, 32, algo="fused").fused
+    assert not B.Plan(6, 32, 64, 64, 56, 56, 1, 64, algo="staged").fused
+    st = B.Plan(6, 32, 64, 64, 56, 56, 1, 64, algo="staged")
+    assert small.workspace_bytes < st.workspace_bytes            # no M buffer when fused
