@@ -129,25 +129,27 @@ constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
 
 // Reduce-scatter steps: pair a[i] with a[i + K/2]; each lane keeps one half
 // (the max over itself and its partner) and returns 1 if it kept the upper half.
-template <int K>
+template <int K, bool ABS = false>
 __device__ __forceinline__ int rs_swap32(float (&a)[64]) {
 #pragma unroll
     for (int i = 0; i < K / 2; ++i) {
         auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[i]), __float_as_uint(a[i + K / 2]),
                                                   false, false);
-        a[i] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        const float p = __uint_as_float(r[0]), q = __uint_as_float(r[1]);
+        a[i] = ABS ? fmaxf(fabsf(p), fabsf(q)) : fmaxf(p, q);
     }
     auto lab = __builtin_amdgcn_permlane32_swap(0u, 1u, false, false);
     return (int)lab[0];
 }
 
-template <int K>
+template <int K, bool ABS = false>
 __device__ __forceinline__ int rs_swap16(float (&a)[64]) {
 #pragma unroll
     for (int i = 0; i < K / 2; ++i) {
         auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(a[i + K / 2]),
                                                   false, false);
-        a[i] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        const float p = __uint_as_float(r[0]), q = __uint_as_float(r[1]);
+        a[i] = ABS ? fmaxf(fabsf(p), fabsf(q)) : fmaxf(p, q);
     }
     auto lab = __builtin_amdgcn_permlane16_swap(0u, 1u, false, false);
     return (int)lab[0];
@@ -155,7 +157,7 @@ __device__ __forceinline__ int rs_swap16(float (&a)[64]) {
 
 // DPP exchange with the lane given by CTRL; BIT is a lane-id bit that differs
 // between partners and decides which half a lane keeps.
-template <int K, int CTRL, int BIT>
+template <int K, int CTRL, int BIT, bool ABS = false>
 __device__ __forceinline__ int rs_dpp(float (&a)[64], int lane) {
     const bool up = (lane >> BIT) & 1;
 #pragma unroll
@@ -163,7 +165,7 @@ __device__ __forceinline__ int rs_dpp(float (&a)[64], int lane) {
         const float lo = a[i], hi = a[i + K / 2];
         const float send = up ? lo : hi, keep = up ? hi : lo;
         const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xf, 0xf, false));
-        a[i] = fmaxf(keep, recv);
+        a[i] = ABS ? fmaxf(fabsf(keep), fabsf(recv)) : fmaxf(keep, recv);
     }
     return up;
 }
@@ -173,27 +175,27 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppXor7 = 0x141;       // row_half_mirror: lane ^ 7 inside 8 lanes
 constexpr int kDppXor8 = 0x128;       // row_ror:8: lane ^ 8 inside 16 lanes
 
-// Max over SEG aligned lanes of 64 values per lane. On return a[j], j < 64/SEG,
-// holds the max for value index base + j (base is returned).
+// Max of |a| over SEG aligned lanes, for 64 values per lane. On return a[j],
+// j < 64/SEG, holds the max for value index base + j (base is returned).
 template <int SEG>
 __device__ __forceinline__ int reduce_scatter_max(float (&a)[64], int lane) {
     int base = 0;
     if constexpr (SEG == 64) {
-        base += rs_swap32<64>(a) * 32;
+        base += rs_swap32<64, true>(a) * 32;
         base += rs_swap16<32>(a) * 16;
         base += rs_dpp<16, kDppXor8, 3>(a, lane) * 8;
         base += rs_dpp<8, kDppXor7, 2>(a, lane) * 4;
         base += rs_dpp<4, kDppXor2, 1>(a, lane) * 2;
         base += rs_dpp<2, kDppXor1, 0>(a, lane);
     } else if constexpr (SEG == 32) {
-        base += rs_swap16<64>(a) * 32;
+        base += rs_swap16<64, true>(a) * 32;
         base += rs_dpp<32, kDppXor8, 3>(a, lane) * 16;
         base += rs_dpp<16, kDppXor7, 2>(a, lane) * 8;
         base += rs_dpp<8, kDppXor2, 1>(a, lane) * 4;
         base += rs_dpp<4, kDppXor1, 0>(a, lane) * 2;
     } else {
         static_assert(SEG == 16, "group lanes must be 16, 32 or 64");
-        base += rs_dpp<64, kDppXor8, 3>(a, lane) * 32;
+        base += rs_dpp<64, kDppXor8, 3, true>(a, lane) * 32;
         base += rs_dpp<32, kDppXor7, 2>(a, lane) * 16;
         base += rs_dpp<16, kDppXor2, 1>(a, lane) * 8;
         base += rs_dpp<8, kDppXor1, 0>(a, lane) * 4;
@@ -201,95 +203,189 @@ __device__ __forceinline__ int reduce_scatter_max(float (&a)[64], int lane) {
     return base;
 }
 
-// n x n patch of one channel: rows outside the image and columns outside it
-// are zero.
-template <int N, bool VEC, typename XT>
-__device__ __forceinline__ void load_patch(const XT *__restrict__ xc, bool ok, int h0, int w0,
-                                           const Geo &g, float (&d)[N][N]) {
+// Stage 1 work item: a strip of TPB horizontally adjacent tiles of one tile
+// row, for CPB input channels. The strip's input window (CPB channels x n rows
+// x WC columns, zero outside the image) is copied to LDS with row-contiguous
+// 16-byte loads (many lanes per window row, so each load instruction touches
+// few cache lines), then each wave reads its tile's n x n patch per channel
+// from LDS. The channel stride in LDS is odd, so those reads (one channel per
+// lane) are free of bank conflicts. (A persistent variant that prefetched the
+// next strip during the arithmetic measured slower than letting two resident
+// blocks per CU overlap on their own.)
+template <int M, int G, int TPB_>
+struct S1Shape {
+    static constexpr int N = M + 2;
+    static constexpr int GW = GroupShape<G>::GW;             // waves per tile
+    static constexpr int TPB = TPB_;
+    static constexpr int NW = TPB * GW;                      // waves per block
+    static constexpr int CPB = 64 * GW;
+    static constexpr int WC = (TPB * M + 2 + 3) / 4 * 4;     // window columns, multiple of 4
+    static constexpr int CS = N * WC + 1;                    // LDS floats per channel (odd)
+    static constexpr int LPS = WC / 4;                       // lanes per window row
+    static constexpr int SPI = 64 / LPS;                     // window rows per wave load
+    static constexpr int SEGS = CPB * N;                     // window rows in the strip
+    static constexpr int ITERS = (SEGS + NW * SPI - 1) / (NW * SPI);
+};
+
+// One thread's share of a strip window in flight between load and LDS.
+template <int M, int G, int TPB>
+struct S1Loads {
+    float f[S1Shape<M, G, TPB>::ITERS][4];
+};
+
+// A work item's position: image, tile row, first tile column, first channel.
+struct S1Item {
+    int img, ty, tx0, c0;
+};
+
+template <int M, int G, int TPB>
+__device__ __forceinline__ S1Item s1_item(int item, const Geo &g) {
+    const int nstrip = (g.tW + TPB - 1) / TPB;
+    const int strip = item % nstrip;
+    const int rem = item / nstrip;
+    const int rows = g.N * g.tH;
+    const int rowid = rem % rows;
+    S1Item it;
+    it.c0 = (rem / rows) * GroupShape<G>::CPB;
+    it.ty = rowid % g.tH;
+    it.img = rowid / g.tH;
+    it.tx0 = strip * TPB;
+    return it;
+}
+
+// Issue all of this thread's window loads for one strip: 4 consecutive
+// columns per lane. A lane whose 4 columns cross the left or right image edge
+// loads the nearest 4 columns inside the image instead (and s1_commit writes
+// them where they belong), so no load starts before the buffer or runs past
+// its end. Rows outside the image and channels past Cin get an offset beyond
+// the buffer end, which a raw buffer load returns as zero. Images narrower
+// than 4 columns load element by element.
+template <int M, int G, int TPB, typename XT>
+__device__ __forceinline__ void s1_issue(S1Loads<M, G, TPB> &ld, __amdgpu_buffer_rsrc_t rx,
+                                         const S1Item &it, const Geo &g) {
+    using SS = S1Shape<M, G, TPB>;
+    auto &f = ld.f;
+    constexpr int ES = sizeof(XT);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int sl = lane / SS::LPS, part = lane - sl * SS::LPS;
+    const int h0 = it.ty * M - g.pad;
+    const int wc = it.tx0 * M - g.pad + 4 * part;
+    const int wl = min(max(wc, 0), g.W - 4);
+    const bool narrow = g.W < 4;  // uniform
+    const int oob = 0x7ffffff0;   // beyond every buffer the plan accepts
 #pragma unroll
-    for (int k = 0; k < N; ++k) {
-        const int h = h0 + k;
-        if (!ok || h < 0 || h >= g.H) {  // uniform except for ok (channel tail)
+    for (int i = 0; i < SS::ITERS; ++i) {
+        const int seg = (i * SS::NW + wave) * SS::SPI + sl;  // window row: (channel, row)
+        const int ch = seg / SS::N, row = seg - ch * SS::N;
+        const int c = it.c0 + ch, h = h0 + row;
+        const bool in = sl < SS::SPI && seg < SS::SEGS && c < g.Cin && h >= 0 && h < g.H;
+        const int rowoff = ((it.img * g.Cin + c) * g.H + h) * g.W;
+        if (!narrow) {
+            const int off = in ? (rowoff + wl) * ES : oob;
+            if constexpr (ES == 4) {
+                const v4i q = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
 #pragma unroll
-            for (int l = 0; l < N; ++l) d[k][l] = 0.0f;
-            continue;
-        }
-        const XT *row = xc + (size_t)h * g.W;
-        if constexpr (VEC) {
-            // W % 4 == 0: 4-float chunks never straddle a row end
-            const int wa = w0 >= 0 ? (w0 & ~3) : -4;
-            const int r = w0 - wa;  // 0..3, uniform
-            float win[12];
-#pragma unroll
-            for (int j = 0; j < 3; ++j) {
-                const int wc = wa + 4 * j;
-                float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (wc >= 0 && wc + 4 <= g.W) f = *(const float4 *)(row + wc);
-                win[4 * j] = f.x;
-                win[4 * j + 1] = f.y;
-                win[4 * j + 2] = f.z;
-                win[4 * j + 3] = f.w;
-            }
-            switch (r) {
-                case 0:
-#pragma unroll
-                    for (int l = 0; l < N; ++l) d[k][l] = win[l];
-                    break;
-                case 1:
-#pragma unroll
-                    for (int l = 0; l < N; ++l) d[k][l] = win[l + 1];
-                    break;
-                case 2:
-#pragma unroll
-                    for (int l = 0; l < N; ++l) d[k][l] = win[l + 2];
-                    break;
-                default:
-#pragma unroll
-                    for (int l = 0; l < N; ++l) d[k][l] = win[l + 3];
-                    break;
+                for (int e = 0; e < 4; ++e) f[i][e] = __int_as_float(q[e]);
+            } else {
+                const auto q = __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 0);
+                f[i][0] = __uint_as_float(q[0] << 16);
+                f[i][1] = __uint_as_float(q[0] & 0xffff0000u);
+                f[i][2] = __uint_as_float(q[1] << 16);
+                f[i][3] = __uint_as_float(q[1] & 0xffff0000u);
             }
         } else {
 #pragma unroll
-            for (int l = 0; l < N; ++l) {
-                const int w = w0 + l;
-                d[k][l] = (w >= 0 && w < g.W) ? load_act(row + w) : 0.0f;
+            for (int e = 0; e < 4; ++e) {
+                const bool ine = in && wc + e >= 0 && wc + e < g.W;
+                const int off = ine ? (rowoff + wc + e) * ES : oob;
+                if constexpr (ES == 4)
+                    f[i][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
+                else
+                    f[i][e] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rx, off, 0, 0) << 16);
             }
         }
     }
 }
 
-template <int M, int G, uint64_t BMASK, bool VEC, typename XT>
-__global__ __launch_bounds__(256) void k_stage1(const XT *__restrict__ x, int8_t *__restrict__ Vq,
-                                                float *__restrict__ sV, Mats mt, Geo g) {
+// Write the loaded columns to the window: at their own columns (wl), plus
+// zeros for this lane's nominal columns that lie outside the image. A column
+// written by two lanes gets the same value from both.
+template <int M, int G, int TPB>
+__device__ __forceinline__ void s1_commit(float *win, S1Loads<M, G, TPB> &ld, const S1Item &it,
+                                          const Geo &g) {
+    using SS = S1Shape<M, G, TPB>;
+    auto &f = ld.f;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int sl = lane / SS::LPS, part = lane - sl * SS::LPS;
+    const int w0 = it.tx0 * M - g.pad;
+    const int wc = w0 + 4 * part;
+    const bool narrow = g.W < 4;
+    const int wl = narrow ? wc : min(max(wc, 0), g.W - 4);
+    const bool clipped = wl != wc;
+#pragma unroll
+    for (int i = 0; i < SS::ITERS; ++i) {
+        const int seg = (i * SS::NW + wave) * SS::SPI + sl;
+        if (sl < SS::SPI && seg < SS::SEGS) {
+            const int ch = seg / SS::N, row = seg - ch * SS::N;
+            float *rowp = win + ch * SS::CS + row * SS::WC;
+            if (clipped) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (wc + e < 0 || wc + e >= g.W) rowp[4 * part + e] = 0.0f;
+            }
+            // window columns of the loaded data; for a clipped lane some lie
+            // before or after its own 4, always inside [0, WC)
+            const int dc = wl - w0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (dc + e >= 0 && dc + e < SS::WC) rowp[dc + e] = f[i][e];
+        }
+    }
+}
+
+template <int M, int G, int TPB, uint64_t BMASK, typename XT>
+__global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW)) void k_stage1(
+    const XT *__restrict__ x, int8_t *__restrict__ Vq, float *__restrict__ sV, Mats mt, Geo g) {
     constexpr int N = M + 2, NT = N * N;
     using S = GroupShape<G>;
+    using SS = S1Shape<M, G, TPB>;
     constexpr int KF = 64 / S::SEG;  // taps per lane after the reduce-scatter
-    __shared__ float red[S::GW > 1 ? 4 : 1][64];
-    __shared__ __attribute__((aligned(16))) float inv_lds[4][64 / S::SEG][64];
+    __shared__ float win[SS::CPB * SS::CS];
+    __shared__ float red[S::GW > 1 ? SS::NW : 1][64];
+    __shared__ __attribute__((aligned(16))) float inv_lds[SS::NW][64 / S::SEG][64];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int c = blockIdx.y * S::CPB + (wave % S::GW) * 64 + lane;
-    const bool cok = c < g.Cin;
+    const int tl = wave / S::GW;                // this wave's tile in the strip
+    const int cl = (wave % S::GW) * 64 + lane;  // this lane's channel in the block
     const int seg = lane / S::SEG;
-    const size_t plane = (size_t)g.T * g.Cin, splane = (size_t)g.T * g.ng;
-    const int ntb = (int)((g.T + S::TPB - 1) / S::TPB);
+    const int n2 = N * N;
+    const int plane = (int)g.T * g.Cin, splane = (int)g.T * g.ng;
+    const auto rx = make_rsrc(x, (size_t)g.N * g.Cin * g.H * g.W * sizeof(XT));
+    const auto rq = make_rsrc(Vq, (size_t)n2 * plane);
+    const auto rs = make_rsrc(sV, (size_t)n2 * splane * 4);
 
-    for (int tb = blockIdx.x; tb < ntb; tb += gridDim.x) {
-        const int t = tb * S::TPB + wave / S::GW;  // uniform per wave
-        const bool tok = t < g.T;
-        const bool ok = tok && cok;
-        int img = 0, ty = 0, tx = 0;
-        if (tok) {
-            tx = t % g.tW;
-            const int r = t / g.tW;
-            ty = r % g.tH;
-            img = r / g.tH;
+    const S1Item cur = s1_item<M, G, TPB>(blockIdx.x, g);
+    {
+        S1Loads<M, G, TPB> f;
+        s1_issue<M, G, TPB, XT>(f, rx, cur, g);
+        s1_commit<M, G, TPB>(win, f, cur, g);
+    }
+    __syncthreads();
+    {
+        const int c = cur.c0 + cl, tx = cur.tx0 + tl;
+        const bool ok = c < g.Cin && tx < g.tW;
+        const int t = (cur.img * g.tH + cur.ty) * g.tW + tx;
+        float d[N][N];
+        {
+            const float *src = win + cl * SS::CS + tl * M;
+#pragma unroll
+            for (int k = 0; k < N; ++k)
+#pragma unroll
+                for (int l = 0; l < N; ++l) d[k][l] = src[k * SS::WC + l];
         }
+
         float v[NT];
         {
-            float d[N][N];
-            const XT *xc = x + ((size_t)img * g.Cin + (cok ? c : 0)) * g.H * g.W;
-            load_patch<N, VEC, XT>(xc, ok, ty * M - g.pad, tx * M - g.pad, g, d);
             float t1[N][N];
 #pragma unroll
             for (int i = 0; i < N; ++i)
@@ -312,9 +408,10 @@ __global__ __launch_bounds__(256) void k_stage1(const XT *__restrict__ x, int8_t
                     v[i * N + j] = acc;
                 }
         }
+        // |v| is taken inside the first reduction step
         float a[64];
 #pragma unroll
-        for (int i = 0; i < 64; ++i) a[i] = i < NT ? fabsf(v[i]) : 0.0f;
+        for (int i = 0; i < 64; ++i) a[i] = i < NT ? v[i] : 0.0f;
         const int base = reduce_scatter_max<S::SEG>(a, lane);
         if constexpr (S::GW > 1) {
 #pragma unroll
@@ -340,11 +437,13 @@ __global__ __launch_bounds__(256) void k_stage1(const XT *__restrict__ x, int8_t
             }
             inv_lds[wave][seg][tap] = inv;
             if (ok && tap < NT && (S::GW == 1 || wave % S::GW == 0))
-                sV[tap * splane + (size_t)t * g.ng + c / G] = sc;
+                // tap differs between lanes, so it goes in the vector offset
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs,
+                                                      (tap * splane + t * g.ng + c / G) * 4, 0, 0);
         }
         __syncthreads();
         if (ok) {
-            int8_t *vp = Vq + (size_t)t * g.Cin + c;
+            const int voff = t * g.Cin + c;
 #pragma unroll
             for (int q4 = 0; q4 < (NT + 3) / 4; ++q4) {
                 const float4 iv = *(const float4 *)&inv_lds[wave][seg][4 * q4];
@@ -354,12 +453,12 @@ __global__ __launch_bounds__(256) void k_stage1(const XT *__restrict__ x, int8_t
                     const int tap = 4 * q4 + e;
                     if (tap < NT) {
                         const float y = v[tap] * ivs[e] + kRoundMagic;
-                        vp[tap * plane] = (int8_t)__float_as_uint(y);
+                        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)__float_as_uint(y), rq, voff,
+                                                             tap * plane, 0);
                     }
                 }
             }
         }
-        __syncthreads();  // inv_lds is rewritten by the next tile
     }
 }
 
@@ -819,15 +918,14 @@ wq8_status launch_weights(const Geo &g, const Mats &mt, const float *w, int8_t *
     return check_launch("weight transform");
 }
 
-template <int M, int G, uint64_t BMASK, bool VEC, typename XT>
+template <int M, int G, int TPB, uint64_t BMASK, typename XT>
 static void stage1_launch(const Geo &g, const Mats &mt, const XT *x, int8_t *Vq, float *sV,
                           hipStream_t s) {
-    using S = GroupShape<G>;
-    const int ntb = (int)((g.T + S::TPB - 1) / S::TPB);
-    const int cblocks = (g.Cin + S::CPB - 1) / S::CPB;
-    // enough blocks for 8 per CU over the 256 CUs, each looping over tiles
-    const int bx = std::max(1, std::min(ntb, (2048 + cblocks - 1) / cblocks));
-    hipLaunchKernelGGL((k_stage1<M, G, BMASK, VEC, XT>), dim3(bx, cblocks), dim3(256), 0, s, x, Vq,
+    using SS = S1Shape<M, G, TPB>;
+    const int nstrip = (g.tW + TPB - 1) / TPB;
+    const int chunks = (g.Cin + SS::CPB - 1) / SS::CPB;
+    const unsigned blocks = (unsigned)(nstrip * g.N * g.tH * chunks);
+    hipLaunchKernelGGL((k_stage1<M, G, TPB, BMASK, XT>), dim3(blocks), dim3(64 * SS::NW), 0, s, x, Vq,
                        sV, mt, g);
 }
 
@@ -835,15 +933,9 @@ template <int M, int G, typename XT>
 static void stage1_m_g(const Geo &g, const Mats &mt, const XT *x, int8_t *Vq, float *sV,
                        hipStream_t s) {
     constexpr uint64_t pat = M == 4 ? kBtPattern4 : kBtPattern6;
-    constexpr bool can_vec = std::is_same<XT, float>::value;
-    const bool vec = can_vec && g.W % 4 == 0;
-    if (g.bt_std) {
-        if (vec) stage1_launch<M, G, pat, can_vec, XT>(g, mt, x, Vq, sV, s);
-        else stage1_launch<M, G, pat, false, XT>(g, mt, x, Vq, sV, s);
-    } else {
-        if (vec) stage1_launch<M, G, ~0ull, can_vec, XT>(g, mt, x, Vq, sV, s);
-        else stage1_launch<M, G, ~0ull, false, XT>(g, mt, x, Vq, sV, s);
-    }
+    constexpr int tpb = 4 / GroupShape<G>::GW;
+    if (g.bt_std) stage1_launch<M, G, tpb, pat, XT>(g, mt, x, Vq, sV, s);
+    else stage1_launch<M, G, tpb, ~0ull, XT>(g, mt, x, Vq, sV, s);
 }
 
 template <int M, typename XT>

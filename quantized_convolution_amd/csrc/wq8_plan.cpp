@@ -325,11 +325,11 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
     // per-tap planes with 32-bit element counts inside a kernel
     const int64_t n2 = (int64_t)n * n;
     const int64_t lim = (int64_t)1 << 31;
-    // the kernels address Vq, sV, Uq, sU and M with 32-bit byte offsets
+    // the kernels address x, y, Vq, sV, Uq, sU and M with 32-bit byte offsets
     if (n2 * g.T * d->Cin >= lim || n2 * g.T * d->Cout * 4 >= lim ||
         n2 * (int64_t)d->Cout * d->Cin >= lim ||
-        (int64_t)d->N * d->Cin * d->H * d->W >= lim * 4 ||
-        (int64_t)d->N * d->Cout * g.Ho * g.Wo >= lim * 4)
+        (int64_t)d->N * d->Cin * d->H * d->W * 4 >= lim ||
+        (int64_t)d->N * d->Cout * g.Ho * g.Wo * 4 >= lim)
         return fail(WQ8_ERR_UNSUPPORTED, "problem too large for this build");
     p->xdt = d->x_dtype;
     p->ydt = d->y_dtype;
