@@ -13,6 +13,9 @@ stream it runs on), and the CPU oracle timed on the host for comparison.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import statistics
@@ -30,6 +33,91 @@ from quantized_convolution_amd import workloads as WL  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POP/s)
+KERNEL_SRC = os.path.join(ROOT, "quantized_convolution_amd", "csrc", "wq8_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# name of each stage's kernel in a rocprofv3 trace (template prefix)
+KERNEL_NAMES = {"stage1": "wq8::k_stage1<", "stage2": "wq8::k_stage2<",
+                "stage3": "wq8::k_stage3<", "stage23": "wq8::k_fused23<"}
+
+
+def kernel_source_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(layer, kernel):
+    """HBM bytes per launch of `kernel` on `layer` from the committed counter
+    summary, or None when there is none or the kernel source has changed
+    since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    k = rec.get("layers", {}).get(layer, {}).get(kernel)
+    return None if k is None else k["bytes_per_launch"]
+
+
+def _pmc_rows(d, counter):
+    """(kernel name, value) of every dispatch in a rocprofv3 --pmc CSV run."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def traffic_summary(layer, fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib):
+    """Turn two counter passes over bench.py (FETCH_SIZE, WRITE_SIZE, KiB per
+    dispatch) and the same two over the copy probe into bytes per launch of
+    each stage kernel. The copy probe reads and writes copy_mib MiB per
+    launch; the counters are scaled by known / counted on it."""
+    known = copy_mib * 2 ** 20
+
+    def copy_factor(d, counter):
+        vals = [v for _, v in _pmc_rows(d, counter)]
+        return known / (statistics.median(vals) * 1024.0)
+
+    fr, wr = copy_factor(cfetch_dir, "FETCH_SIZE"), copy_factor(cwrite_dir, "WRITE_SIZE")
+    out = {"kernel_source_sha": kernel_source_sha(), "copy_probe_mib": copy_mib,
+           "fetch_factor": round(fr, 4), "write_factor": round(wr, 4), "layers": {layer: {}}}
+    fetch, write = _pmc_rows(fetch_dir, "FETCH_SIZE"), _pmc_rows(write_dir, "WRITE_SIZE")
+    lines = ["| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (scaled) |",
+             "|---|---|---|---|---|"]
+    for stage, prefix in KERNEL_NAMES.items():
+        f = [v for k, v in fetch if prefix in k]
+        w = [v for k, v in write if prefix in k]
+        if not f or not w:
+            continue
+        fk, wk = statistics.median(f), statistics.median(w)
+        b = int(round(fk * 1024 * fr + wk * 1024 * wr))
+        out["layers"][layer][stage] = {"fetch_kib": fk, "write_kib": wk, "bytes_per_launch": b}
+        lines.append(f"| {stage} | {len(f)} | {fk:.1f} | {wk:.1f} | {b} |")
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"copy probe {copy_mib} MiB: fetch factor {fr:.4f}, write factor {wr:.4f}")
+    print("\n".join(lines))
+
+
+def copy_probe(mib, steps, dev):
+    """A plain copy kernel of known size (read mib MiB, write mib MiB per
+    launch) for calibrating the HBM byte counters."""
+    n = mib * 2 ** 20 // 4
+    src = torch.empty(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    for _ in range(steps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_mib": mib, "launches": steps}), flush=True)
 
 
 def stage_bytes(L, plan):
@@ -142,13 +230,25 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="one line per layer and schedule (for tuning; no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, metavar="MIB",
+                    help="only run a copy kernel of MIB MiB (counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
+                    help="rocprofv3 --pmc output dirs (bench FETCH_SIZE, bench WRITE_SIZE, copy "
+                         "probe FETCH_SIZE, copy probe WRITE_SIZE): write profiles/traffic.json")
+    ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args.layer, *args.traffic_summary, args.copy_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is not "
               "sharded across GPUs in this build", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps, dev)
+        return
 
     if args.sweep:
         for name, L in WL.LAYERS.items():
@@ -172,7 +272,8 @@ def main():
                    "schedule": "fused" if plan.fused else "staged"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(r["achieved"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(r["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(L.name, dom),
                      "bytes_per_launch": r["nbytes"][dom]},
         "stages": r["stages"],
         "wall_s": round(r["wall"], 3),

@@ -25,6 +25,8 @@ struct Geo {
     int64_t T;                // tiles
     int bt_std, at_std;       // 1 if B^T / A^T vanish wherever the standard
                               // points' matrices do (zero terms may be skipped)
+    int co_major;             // fused kernel: 1 = output-channel blocks outermost
+                              // (weights larger than the activation codes)
 };
 
 // Nonzero patterns of B^T [n][n] and A^T [m][n] for the standard points

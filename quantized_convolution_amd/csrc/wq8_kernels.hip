@@ -26,6 +26,16 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // 64-bit address has to be kept live. The plan keeps every array below 2^31
 // bytes, so 32-bit offsets cover them.
 constexpr int kBufferFlags = 0x00020000;  // gfx9 dword 3: 32-bit raw buffer
+// The dispatcher hands workgroup b to XCD b % 8, and each XCD has its own L2.
+// Renumbering so that XCD x runs one contiguous range of logical blocks puts
+// neighbouring work items (which share input rows or operand panels) behind
+// the same L2. The map is a bijection on [0, nb) for any nb.
+__device__ __forceinline__ int xcd_block(int b, int nb) {
+    constexpr int kXcd = 8;
+    const int q = nb / kXcd, r = nb % kXcd, x = b % kXcd;
+    return x * q + min(x, r) + b / kXcd;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, size_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, kBufferFlags);
 }
@@ -364,7 +374,7 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW)) void k_stage1(
     const auto rq = make_rsrc(Vq, (size_t)n2 * plane);
     const auto rs = make_rsrc(sV, (size_t)n2 * splane * 4);
 
-    const S1Item cur = s1_item<M, G, TPB>(blockIdx.x, g);
+    const S1Item cur = s1_item<M, G, TPB>(xcd_block(blockIdx.x, gridDim.x), g);
     {
         S1Loads<M, G, TPB> f;
         s1_issue<M, G, TPB, XT>(f, rx, cur, g);
@@ -710,7 +720,10 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, kq = lane >> 4;
     const int nco = (g.Cout + 15) / 16;
-    const int cob = blockIdx.x % nco, tb = blockIdx.x / nco;
+    const int blk = xcd_block(blockIdx.x, gridDim.x);
+    const int ntb = (int)((g.T + 15) / 16);
+    const int cob = g.co_major ? blk / ntb : blk % nco;
+    const int tb = g.co_major ? blk % ntb : blk / nco;
     const int t0 = tb * 16, co0 = cob * 16;
     const int tap0 = wave * TPW;
     const size_t vplane = (size_t)g.T * g.Cin, uplane = (size_t)g.Cout * g.Cin;

@@ -419,6 +419,10 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
         p->fused = d->algo == WQ8_ALGO_FUSED;
     }
     p->ws_bytes = p->fused ? p->off_m : p->off_m + (size_t)(n2 * g.T * g.Cout) * 4;
+    // every output-channel block reads all activation codes of its tiles and
+    // every tile block all weights of its channels: keep the larger operand
+    // split across the XCDs' L2s
+    p->geo.co_major = p->u_code_bytes > (size_t)(n2 * g.T * g.Cin);
     return WQ8_OK;
 }
 
