@@ -215,13 +215,18 @@ __device__ __forceinline__ int reduce_scatter_max(float (&a)[64], int lane) {
 
 // Stage 1 work item: a strip of TPB horizontally adjacent tiles of one tile
 // row, for CPB input channels. The strip's input window (CPB channels x n rows
-// x WC columns, zero outside the image) is copied to LDS with row-contiguous
-// 16-byte loads (many lanes per window row, so each load instruction touches
-// few cache lines), then each wave reads its tile's n x n patch per channel
-// from LDS. The channel stride in LDS is odd, so those reads (one channel per
-// lane) are free of bank conflicts. (A persistent variant that prefetched the
-// next strip during the arithmetic measured slower than letting two resident
-// blocks per CU overlap on their own.)
+// x WC columns, zero outside the image) is copied to LDS, then each wave reads
+// its tile's n x n patch per channel from LDS (one channel per lane; the
+// channel stride in LDS is odd, so these reads are free of bank conflicts).
+//
+// The window starts at the 4-aligned column at or before the strip's first
+// input column, so every lane loads an aligned quad of 4 columns. When W is a
+// multiple of 4 such a quad lies wholly inside or wholly outside the image
+// and is one 16-byte (bf16: 8-byte) load; otherwise each column is loaded on
+// its own. One load instruction covers CPI channels x QPR quads of one window
+// row; which row and channels is the same for all lanes, so that part of the
+// address, and the zero fill of rows outside the image, go in the scalar
+// offset (a raw buffer load returns zero past the buffer's end).
 template <int M, int G, int TPB_>
 struct S1Shape {
     static constexpr int N = M + 2;
@@ -229,12 +234,14 @@ struct S1Shape {
     static constexpr int TPB = TPB_;
     static constexpr int NW = TPB * GW;                      // waves per block
     static constexpr int CPB = 64 * GW;
-    static constexpr int WC = (TPB * M + 2 + 3) / 4 * 4;     // window columns, multiple of 4
+    static constexpr int NEED = 3 + TPB * M + 2;             // window columns used, at most
+    static constexpr int QPR = NEED <= 8 ? 2 : NEED <= 16 ? 4 : 8;  // quads per window row
+    static constexpr int WC = 4 * QPR;
+    static constexpr int CPI = 64 / QPR;                     // channels per load instruction
     static constexpr int CS = N * WC + 1;                    // LDS floats per channel (odd)
-    static constexpr int LPS = WC / 4;                       // lanes per window row
-    static constexpr int SPI = 64 / LPS;                     // window rows per wave load
-    static constexpr int SEGS = CPB * N;                     // window rows in the strip
-    static constexpr int ITERS = (SEGS + NW * SPI - 1) / (NW * SPI);
+    static constexpr int ITERS = CPB / CPI * N / NW;         // load instructions per wave
+    static_assert(NEED <= WC && ITERS * NW * CPI == CPB * N, "stage-1 window shape");
+    static_assert(16 % CPI == 0, "a load instruction must not straddle a channel group");
 };
 
 // One thread's share of a strip window in flight between load and LDS.
@@ -263,41 +270,46 @@ __device__ __forceinline__ S1Item s1_item(int item, const Geo &g) {
     return it;
 }
 
-// Issue all of this thread's window loads for one strip: 4 consecutive
-// columns per lane. A lane whose 4 columns cross the left or right image edge
-// loads the nearest 4 columns inside the image instead (and s1_commit writes
-// them where they belong), so no load starts before the buffer or runs past
-// its end. Rows outside the image and channels past Cin get an offset beyond
-// the buffer end, which a raw buffer load returns as zero. Images narrower
-// than 4 columns load element by element.
-template <int M, int G, int TPB, typename XT>
+// First window column (4-aligned, may be negative) of a work item.
+template <int M>
+__device__ __forceinline__ int s1_w0(const S1Item &it, const Geo &g) {
+    return ((it.tx0 * M - g.pad) >> 2) << 2;  // arithmetic shift: floor
+}
+
+// Issue all of this thread's window loads for one strip.
+template <int M, int G, int TPB, bool VEC, typename XT>
 __device__ __forceinline__ void s1_issue(S1Loads<M, G, TPB> &ld, __amdgpu_buffer_rsrc_t rx,
-                                         const S1Item &it, const Geo &g) {
+                                         const S1Item &it, const Geo &g, int wave) {
     using SS = S1Shape<M, G, TPB>;
     auto &f = ld.f;
     constexpr int ES = sizeof(XT);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int sl = lane / SS::LPS, part = lane - sl * SS::LPS;
+    constexpr int OOB = 0x7ffffff0;  // beyond every buffer the plan accepts; two sum below 2^32
+    const int lane = threadIdx.x & 63;
+    const int chs = lane / SS::QPR, part = lane % SS::QPR;
+    const int col = s1_w0<M>(it, g) + 4 * part;
+    const int hw = g.H * g.W;
     const int h0 = it.ty * M - g.pad;
-    const int wc = it.tx0 * M - g.pad + 4 * part;
-    const int wl = min(max(wc, 0), g.W - 4);
-    const bool narrow = g.W < 4;  // uniform
-    const int oob = 0x7ffffff0;   // beyond every buffer the plan accepts
+    const int lrow = (it.img * g.Cin + it.c0 + chs) * hw;  // this lane's channel plane
+    int vb[VEC ? 1 : 4];
+    if constexpr (VEC) {
+        vb[0] = col >= 0 && col < g.W ? (lrow + col) * ES : OOB;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vb[e] = col + e >= 0 && col + e < g.W ? (lrow + col + e) * ES : OOB;
+    }
 #pragma unroll
     for (int i = 0; i < SS::ITERS; ++i) {
-        const int seg = (i * SS::NW + wave) * SS::SPI + sl;  // window row: (channel, row)
-        const int ch = seg / SS::N, row = seg - ch * SS::N;
-        const int c = it.c0 + ch, h = h0 + row;
-        const bool in = sl < SS::SPI && seg < SS::SEGS && c < g.Cin && h >= 0 && h < g.H;
-        const int rowoff = ((it.img * g.Cin + c) * g.H + h) * g.W;
-        if (!narrow) {
-            const int off = in ? (rowoff + wl) * ES : oob;
+        const int j = i * SS::NW + wave;  // uniform: window row and channel slice
+        const int row = j % SS::N, cho = (j / SS::N) * SS::CPI;
+        const int h = h0 + row;
+        const int so = h >= 0 && h < g.H && it.c0 + cho < g.Cin ? (cho * hw + h * g.W) * ES : OOB;
+        if constexpr (VEC) {
             if constexpr (ES == 4) {
-                const v4i q = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+                const v4i q = __builtin_amdgcn_raw_buffer_load_b128(rx, vb[0], so, 0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) f[i][e] = __int_as_float(q[e]);
             } else {
-                const auto q = __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 0);
+                const auto q = __builtin_amdgcn_raw_buffer_load_b64(rx, vb[0], so, 0);
                 f[i][0] = __uint_as_float(q[0] << 16);
                 f[i][1] = __uint_as_float(q[0] & 0xffff0000u);
                 f[i][2] = __uint_as_float(q[1] << 16);
@@ -306,54 +318,33 @@ __device__ __forceinline__ void s1_issue(S1Loads<M, G, TPB> &ld, __amdgpu_buffer
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const bool ine = in && wc + e >= 0 && wc + e < g.W;
-                const int off = ine ? (rowoff + wc + e) * ES : oob;
                 if constexpr (ES == 4)
-                    f[i][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
+                    f[i][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, vb[e], so, 0));
                 else
-                    f[i][e] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rx, off, 0, 0) << 16);
+                    f[i][e] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rx, vb[e], so, 0)
+                                              << 16);
             }
         }
     }
 }
 
-// Write the loaded columns to the window: at their own columns (wl), plus
-// zeros for this lane's nominal columns that lie outside the image. A column
-// written by two lanes gets the same value from both.
+// Write the loaded quads to the LDS window.
 template <int M, int G, int TPB>
-__device__ __forceinline__ void s1_commit(float *win, S1Loads<M, G, TPB> &ld, const S1Item &it,
-                                          const Geo &g) {
+__device__ __forceinline__ void s1_commit(float *win, const S1Loads<M, G, TPB> &ld, int wave) {
     using SS = S1Shape<M, G, TPB>;
-    auto &f = ld.f;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int sl = lane / SS::LPS, part = lane - sl * SS::LPS;
-    const int w0 = it.tx0 * M - g.pad;
-    const int wc = w0 + 4 * part;
-    const bool narrow = g.W < 4;
-    const int wl = narrow ? wc : min(max(wc, 0), g.W - 4);
-    const bool clipped = wl != wc;
+    const int lane = threadIdx.x & 63;
+    float *lp = win + (lane / SS::QPR) * SS::CS + 4 * (lane % SS::QPR);
 #pragma unroll
     for (int i = 0; i < SS::ITERS; ++i) {
-        const int seg = (i * SS::NW + wave) * SS::SPI + sl;
-        if (sl < SS::SPI && seg < SS::SEGS) {
-            const int ch = seg / SS::N, row = seg - ch * SS::N;
-            float *rowp = win + ch * SS::CS + row * SS::WC;
-            if (clipped) {
+        const int j = i * SS::NW + wave;
+        const int row = j % SS::N, cho = (j / SS::N) * SS::CPI;
+        float *p = lp + cho * SS::CS + row * SS::WC;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (wc + e < 0 || wc + e >= g.W) rowp[4 * part + e] = 0.0f;
-            }
-            // window columns of the loaded data; for a clipped lane some lie
-            // before or after its own 4, always inside [0, WC)
-            const int dc = wl - w0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (dc + e >= 0 && dc + e < SS::WC) rowp[dc + e] = f[i][e];
-        }
+        for (int e = 0; e < 4; ++e) p[e] = ld.f[i][e];
     }
 }
 
-template <int M, int G, int TPB, uint64_t BMASK, typename XT>
+template <int M, int G, int TPB, uint64_t BMASK, bool VEC, typename XT>
 __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW)) void k_stage1(
     const XT *__restrict__ x, int8_t *__restrict__ Vq, float *__restrict__ sV, Mats mt, Geo g) {
     constexpr int N = M + 2, NT = N * N;
@@ -377,8 +368,8 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW)) void k_stage1(
     const S1Item cur = s1_item<M, G, TPB>(xcd_block(blockIdx.x, gridDim.x), g);
     {
         S1Loads<M, G, TPB> f;
-        s1_issue<M, G, TPB, XT>(f, rx, cur, g);
-        s1_commit<M, G, TPB>(win, f, cur, g);
+        s1_issue<M, G, TPB, VEC, XT>(f, rx, cur, g, wave);
+        s1_commit<M, G, TPB>(win, f, wave);
     }
     __syncthreads();
     {
@@ -387,7 +378,7 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW)) void k_stage1(
         const int t = (cur.img * g.tH + cur.ty) * g.tW + tx;
         float d[N][N];
         {
-            const float *src = win + cl * SS::CS + tl * M;
+            const float *src = win + cl * SS::CS + (cur.tx0 * M - g.pad - s1_w0<M>(cur, g)) + tl * M;
 #pragma unroll
             for (int k = 0; k < N; ++k)
 #pragma unroll
@@ -938,15 +929,20 @@ static void stage1_launch(const Geo &g, const Mats &mt, const XT *x, int8_t *Vq,
     const int nstrip = (g.tW + TPB - 1) / TPB;
     const int chunks = (g.Cin + SS::CPB - 1) / SS::CPB;
     const unsigned blocks = (unsigned)(nstrip * g.N * g.tH * chunks);
-    hipLaunchKernelGGL((k_stage1<M, G, TPB, BMASK, XT>), dim3(blocks), dim3(64 * SS::NW), 0, s, x, Vq,
-                       sV, mt, g);
+    if (g.W % 4 == 0)
+        hipLaunchKernelGGL((k_stage1<M, G, TPB, BMASK, true, XT>), dim3(blocks), dim3(64 * SS::NW), 0, s,
+                           x, Vq, sV, mt, g);
+    else
+        hipLaunchKernelGGL((k_stage1<M, G, TPB, BMASK, false, XT>), dim3(blocks), dim3(64 * SS::NW), 0,
+                           s, x, Vq, sV, mt, g);
 }
 
 template <int M, int G, typename XT>
 static void stage1_m_g(const Geo &g, const Mats &mt, const XT *x, int8_t *Vq, float *sV,
                        hipStream_t s) {
     constexpr uint64_t pat = M == 4 ? kBtPattern4 : kBtPattern6;
-    constexpr int tpb = 4 / GroupShape<G>::GW;
+    // tiles per block: 4 (one wave each) up to 128-channel groups; 1 for 256
+    constexpr int tpb = GroupShape<G>::GW <= 2 ? 4 : 1;
     if (g.bt_std) stage1_launch<M, G, tpb, pat, XT>(g, mt, x, Vq, sV, s);
     else stage1_launch<M, G, tpb, ~0ull, XT>(g, mt, x, Vq, sV, s);
 }
