@@ -15,6 +15,7 @@ struct Mats {
     float Bt[kMaxN * kMaxN];  // [n][n]  carries S_B
     float G[kMaxN * 3];       // [n][3]  carries S_G
     float At[6 * kMaxN];      // [m][n]  carries S_A
+    float kscale, oscale;     // 2^-s and 2^s with max |A^T (x) A^T| * 2^-s <= 2^14
 };
 
 // Problem geometry shared by every kernel.

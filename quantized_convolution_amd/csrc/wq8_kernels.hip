@@ -26,6 +26,10 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // 64-bit address has to be kept live. The plan keeps every array below 2^31
 // bytes, so 32-bit offsets cover them.
 constexpr int kBufferFlags = 0x00020000;  // gfx9 dword 3: 32-bit raw buffer
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, size_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, kBufferFlags);
+}
+
 // The dispatcher hands workgroup b to XCD b % 8, and each XCD has its own L2.
 // Renumbering so that XCD x runs one contiguous range of logical blocks puts
 // neighbouring work items (which share input rows or operand panels) behind
@@ -34,10 +38,6 @@ __device__ __forceinline__ int xcd_block(int b, int nb) {
     constexpr int kXcd = 8;
     const int q = nb / kXcd, r = nb % kXcd, x = b % kXcd;
     return x * q + min(x, r) + b / kXcd;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, size_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, kBufferFlags);
 }
 
 // ----------------------------------------------------------------- helpers
@@ -684,31 +684,58 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
 
 // ------------------------------------------------- fused stages 2 + 3
 // The Winograd-domain output M never leaves the chip. A block owns 16 tiles x
-// 16 output channels and all n*n taps; wave w computes taps
-// [w*NT/4, (w+1)*NT/4) of that 16 x 16 block on MFMA with U as the A operand
-// (rows = output channels) and V as the B operand (columns = tiles), so lane
-// (r, kq) ends with the four (co = 4kq + i, t = r) pairs for its taps. The
-// per-group dequantization is the same fma chain over groups as stage 2. The
-// Y absmax over all taps of a pair combines the four waves' partial maxima
-// through LDS; the rounded codes go to LDS, and in the epilogue each lane
-// takes one (tile, co) pair and applies A^T Yq A (fp32 fma chains in index
-// order, structurally zero A^T terms skipped) and the scale.
-template <int M, int G, uint64_t AMASK, typename YT>
+// 16 output channels (256 (tile, co) pairs) and all n*n taps.
+//
+// Hadamard part: wave w computes taps [w*NT/4, (w+1)*NT/4) of the 16 x 16
+// block on int8 MFMA with U as the A operand (rows = output channels) and V as
+// the B operand (columns = tiles), so lane (r, kq) ends with the four
+// (co = 4kq + i, t = r) pairs for its taps. The per-group dequantization is
+// the same fma chain over groups as stage 2, so M is bit-identical to it.
+//
+// Y: the absmax of a pair over all taps combines the four waves' partial
+// maxima through LDS; one thread per pair computes 127/a and a/127 (the same
+// IEEE divisions as stage 3) and the codes are rounded by the wave that holds
+// the values. Codes are small integers, exact in fp16, and go to LDS as fp16.
+//
+// Output transform: for each pair, vec(O) = (A^T (x) A^T) vec(Yq), one dense
+// [m*m] x [n*n] product for all 256 pairs of the block, on fp16 MFMA
+// (16x16x32, fp32 accumulation). The Kronecker matrix K (built per block in
+// LDS from A^T) is scaled by a power of two and split into fp16 high and low
+// parts, K = Kh + Kl, so Kh*Yq + Kl*Yq carries about 22 significant bits of
+// K: the result differs from an fp32 evaluation of A^T Yq A by ~1e-6 of its
+// RMS, well inside the tolerance of the output (which, unlike the codes, is
+// not required to be bit-exact).
+//
+// LDS rows of 64 fp16 (one pair's codes, or one row of K) are 128 bytes; the
+// 16-byte chunk c of row p is stored at chunk c ^ ((p >> 1) & 7), which makes
+// the 16-lane 16-byte reads and writes below free of bank conflicts.
+__device__ __forceinline__ int swz(int row, int chunk) { return (row << 6) + ((chunk ^ ((row >> 1) & 7)) << 3); }
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+template <int M, int G, int GC, typename YT>
 __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
                                                  const float *__restrict__ sV,
                                                  const int8_t *__restrict__ Uq,
                                                  const float *__restrict__ sU, YT *__restrict__ y,
                                                  Mats mt, Geo g) {
     constexpr int N = M + 2, NT = N * N, TPW = NT / 4;
+    constexpr int BS = M == 6 ? 8 : 4;  // output row a, column b -> product row a * BS + b
+    constexpr int MR = M * BS, RB = MR / 16;  // rows and 16-row blocks of the output product
     constexpr bool K64 = G % 64 == 0;
     constexpr int KSTEPS = K64 ? G / 64 : 1;
-    constexpr int PST = NT + 4;  // padded pair stride in LDS (floats)
-    __shared__ __attribute__((aligned(16))) float codes[256 * PST];
+    constexpr int ES = sizeof(YT);
+    static_assert(NT <= 64 && TPW * 4 == NT && TPW <= 16, "taps per wave");
+    __shared__ __attribute__((aligned(16))) _Float16 codes[256 * 64];
+    __shared__ __attribute__((aligned(16))) _Float16 ktab[2][MR * 64];
     __shared__ float pmax[4][256];
-    __shared__ float sy_lds[256];
+    __shared__ float s_inv[256], s_out[256];
+    __shared__ float at_lds[M * N];
 
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
     const int nco = (g.Cout + 15) / 16;
     const int blk = xcd_block(blockIdx.x, gridDim.x);
@@ -718,6 +745,7 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
     const int t0 = tb * 16, co0 = cob * 16;
     const int tap0 = wave * TPW;
     const size_t vplane = (size_t)g.T * g.Cin, uplane = (size_t)g.Cout * g.Cin;
+    if (tid < M * N) at_lds[tid] = mt.At[tid];
 
     // ---- Hadamard GEMMs for this wave's taps
     // Rows past T or Cout read row 0 instead: they only feed (tile, co) pairs
@@ -736,13 +764,6 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
     const int koff = K64 ? 16 * kq : (kin ? 8 * kq : 0);
     const int voff = tBc * g.Cin + koff;
     const int uoff = coAc * g.Cin + koff;
-    const int svoff = tBc * g.ng * 4;
-    int suoff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int co = co0 + 4 * kq + i;
-        suoff[i] = (co < g.Cout ? co : 0) * g.ng * 4;
-    }
     float acc[TPW][4];
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
@@ -752,7 +773,6 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
     // Operands of one tap for one group.
     struct TapOps {
         v4i a[K64 ? KSTEPS : 1], b[K64 ? KSTEPS : 1];
-        float sv, su[4];
     };
     auto load_tap = [&](int j, int gi, TapOps &o) {
         const int tap = tap0 + j;
@@ -769,14 +789,38 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
             o.a[0] = v4i{(int)a2[0], (int)a2[1], 0, 0};
             o.b[0] = v4i{(int)b2[0], (int)b2[1], 0, 0};
         }
-        o.sv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsV, svoff,
-                                                                    (tap * (int)g.T * g.ng + gi) * 4, 0));
-        const int su_s = (tap * g.Cout * g.ng + gi) * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            o.su[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsU, suoff[i], su_s, 0));
     };
-    auto use_tap = [&](int j, const TapOps &o) {
+    // Group scales of this wave's taps for GC groups at a time, staged in LDS
+    // (in the code area, idle until the Hadamard part ends) with a few wide
+    // loads: sv[j][gg][tile row], su[j][gg][channel row]; 8 KB per wave.
+    float *scl = reinterpret_cast<float *>(codes) + wave * (2 * 16 * GC * 16);
+    auto stage_scales = [&](int g0) {
+        // lane slot e = 64k + lane: k < 4 -> sv, else su; tap j = (e / 16) % 16; row = lane % 16
+        float sreg[8][GC];
+        const int row = lane & 15;
+        const int tr = t0 + row < g.T ? t0 + row : 0, cr = co0 + row < g.Cout ? co0 + row : 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int j = (4 * k + (lane >> 4)) & 15;
+            const int tap = tap0 + (j < TPW ? j : 0);
+            const auto rs = k < 4 ? rsV : rsU;
+            const int off = k < 4 ? ((tap * (int)g.T + tr) * g.ng + g0) * 4 : ((tap * g.Cout + cr) * g.ng + g0) * 4;
+            if constexpr (GC == 4) {
+                const v4i q = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sreg[k][u] = __int_as_float(q[u]);
+            } else {
+                sreg[k][0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int j = (4 * k + (lane >> 4)) & 15;
+#pragma unroll
+            for (int u = 0; u < GC; ++u) scl[(((k >> 2) * 16 + j) * GC + u) * 16 + row] = sreg[k][u];
+        }
+    };
+    auto use_tap = [&](int j, int gg, const TapOps &o) {
         v4i P = v4i{0, 0, 0, 0};
         if constexpr (K64) {
 #pragma unroll
@@ -790,9 +834,12 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
             b = kin ? b : 0;
             P = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, P, 0, 0, 0);
         }
+        const float sv = scl[(j * GC + gg) * 16 + r];
+        const float4 su = *(const float4 *)&scl[((16 + j) * GC + gg) * 16 + 4 * kq];
+        const float sus[4] = {su.x, su.y, su.z, su.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float sc = o.sv * o.su[i];
+            const float sc = sv * sus[i];
             acc[j][i] = __builtin_fmaf(sc, (float)P[i], acc[j][i]);
         }
     };
@@ -800,24 +847,28 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
     // the current batch's MFMAs and dequantization
     constexpr int BATCH = KSTEPS >= 4 ? 1 : KSTEPS == 2 ? (TPW % 2 == 0 ? 2 : 3)
                                                         : (TPW % 4 == 0 ? 4 : 3);
-    for (int gi = 0; gi < g.ng; ++gi) {
-        TapOps buf[2][BATCH];
+    for (int g0 = 0; g0 < g.ng; g0 += GC) {
+        stage_scales(g0);
+        const int gend = g0 + GC < g.ng ? g0 + GC : g.ng;
+        for (int gi = g0; gi < gend; ++gi) {
+            TapOps buf[2][BATCH];
 #pragma unroll
-        for (int b = 0; b < BATCH; ++b) load_tap(b, gi, buf[0][b]);
+            for (int b = 0; b < BATCH; ++b) load_tap(b, gi, buf[0][b]);
 #pragma unroll
-        for (int jb = 0; jb < TPW; jb += BATCH) {
-            const int cur = (jb / BATCH) & 1;
-            if (jb + BATCH < TPW)
+            for (int jb = 0; jb < TPW; jb += BATCH) {
+                const int cur = (jb / BATCH) & 1;
+                if (jb + BATCH < TPW)
 #pragma unroll
-                for (int b = 0; b < BATCH; ++b) load_tap(jb + BATCH + b, gi, buf[cur ^ 1][b]);
-            __builtin_amdgcn_sched_barrier(0);
+                    for (int b = 0; b < BATCH; ++b) load_tap(jb + BATCH + b, gi, buf[cur ^ 1][b]);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int b = 0; b < BATCH; ++b) use_tap(jb + b, buf[cur][b]);
-            __builtin_amdgcn_sched_barrier(0);
+                for (int b = 0; b < BATCH; ++b) use_tap(jb + b, gi - g0, buf[cur][b]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 
-    // ---- Y: one scale per (tile, co) over all taps
+    // ---- Y absmax per pair: partial maxima of this wave's taps
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float m = 0.0f;
@@ -826,63 +877,150 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
         pmax[wave][(4 * kq + i) * 16 + r] = m;
     }
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = (4 * kq + i) * 16 + r;
-        const float am = fmaxf(fmaxf(pmax[0][p], pmax[1][p]), fmaxf(pmax[2][p], pmax[3][p]));
+    {
+        // one thread per pair: the scales. K in LDS: row ab, 8 taps per task.
+        const float am = fmaxf(fmaxf(pmax[0][tid], pmax[1][tid]), fmaxf(pmax[2][tid], pmax[3][tid]));
         float inv = 0.0f, sy = 0.0f;
         if (am != 0.0f) {
             inv = 127.0f / am;
             sy = am / 127.0f;
         }
-        if (wave == 0) sy_lds[p] = sy;
-        float *cp = codes + p * PST + tap0;
+        s_inv[tid] = inv;
+        s_out[tid] = sy * mt.oscale;
+        for (int task = tid; task < MR * 8; task += 256) {
+            const int row = task >> 3, c = task & 7;
+            const int a = row / BS, b = row % BS;
+            h8 hi, lo;
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) cp[j] = __builtin_rintf(acc[j][i] * inv);
+            for (int u = 0; u < 8; ++u) {
+                const int tap = 8 * c + u;
+                float kv = 0.0f;
+                if (tap < NT && b < M) {
+                    const int i = tap / N, j = tap - (tap / N) * N;
+                    kv = (at_lds[a * N + i] * mt.kscale) * at_lds[b * N + j];
+                }
+                const _Float16 h = (_Float16)kv;
+                hi[u] = h;
+                lo[u] = (_Float16)(kv - (float)h);
+            }
+            *(h8 *)&ktab[0][swz(row, c)] = hi;
+            *(h8 *)&ktab[1][swz(row, c)] = lo;
+        }
+    }
+    __syncthreads();
+    // ---- codes of this wave's taps, fp16, into the pair rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = (4 * kq + i) * 16 + r;
+        const float inv = s_inv[p];
+        if constexpr (TPW % 8 == 0) {
+#pragma unroll
+            for (int c = 0; c < TPW / 8; ++c) {
+                h8 q;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) q[u] = (_Float16)__builtin_rintf(acc[8 * c + u][i] * inv);
+                *(h8 *)&codes[swz(p, tap0 / 8 + c)] = q;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                const int tap = tap0 + j;
+                codes[swz(p, tap >> 3) + (tap & 7)] = (_Float16)__builtin_rintf(acc[j][i] * inv);
+            }
+        }
+    }
+    if constexpr (NT < 64) {
+        // taps NT..63 of every pair row: zero (K is zero there; keep B finite)
+        for (int tap = NT; tap < 64; ++tap) codes[swz(tid, tap >> 3) + (tap & 7)] = (_Float16)0.0f;
     }
     __syncthreads();
 
-    // ---- output transform, one (tile, co) pair per lane
-    const int p = wave * 64 + lane;
-    const int tl = p & 15, col = p >> 4;
-    const int t = t0 + tl, co = co0 + col;
-    if (t >= g.T || co >= g.Cout) return;
-    float q[NT];
-    const float *cp = codes + p * PST;
+    // ---- output transform: D[ab][pair] = sum_tap K[ab][tap] * Yq[tap][pair]
+    // Wave w takes pairs 64w .. 64w+63 (4 column blocks of 16 = tiles t0..t0+15
+    // of output channel co0 + 4w + cb). Lane (kg = lane / 16, nl = lane % 16).
+    const int kg = lane >> 4, nl = lane & 15;
+    h8 bq[4][2];
 #pragma unroll
-    for (int k = 0; k < NT / 4; ++k) {
-        const float4 f = *(const float4 *)(cp + 4 * k);
-        q[4 * k] = f.x;
-        q[4 * k + 1] = f.y;
-        q[4 * k + 2] = f.z;
-        q[4 * k + 3] = f.w;
-    }
-    const float sy = sy_lds[p];
-    float z[M][N];
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-    for (int a = 0; a < M; ++a)
+        for (int ks = 0; ks < 2; ++ks) bq[cb][ks] = *(const h8 *)&codes[swz(64 * wave + 16 * cb + nl, 4 * ks + kg)];
+    float so[4];
 #pragma unroll
-        for (int j = 0; j < N; ++j) {
-            float acc2 = 0.0f;
+    for (int cb = 0; cb < 4; ++cb) so[cb] = s_out[64 * wave + 16 * cb + nl];
+
+    // This lane's tile; per row block, the output pixel (a, b0) of its first
+    // row 16rb + 4kg and how many of its 4 adjacent pixels b0..b0+3 are inside
+    // the image (rows a * BS + b with b >= m are padding).
+    const int t = t0 + nl;
+    int ooff[RB], nv[RB];
+    {
+        const int tx = t % g.tW, rr = t / g.tW, ty = rr % g.tH, img = rr / g.tH;
+        const int hv = g.Ho - ty * M, wv = g.Wo - tx * M;
+        const int base = (img * g.Cout * g.Ho + ty * M) * g.Wo + tx * M;
 #pragma unroll
-            for (int i = 0; i < N; ++i)
-                if ((AMASK >> (a * N + i)) & 1) acc2 = __builtin_fmaf(mt.At[a * N + i], q[i * N + j], acc2);
-            z[a][j] = acc2;
+        for (int rb = 0; rb < RB; ++rb) {
+            const int row0 = 16 * rb + 4 * kg;
+            const int a = row0 / BS, b0 = row0 % BS;
+            const int n = min(4, min(M, wv) - b0);
+            nv[rb] = t < g.T && a < hv && n > 0 ? n : 0;
+            ooff[rb] = (base + a * g.Wo + b0) * ES;
         }
-    const int tx = t % g.tW, rr = t / g.tW, ty = rr % g.tH, img = rr / g.tH;
-    YT *yp = y + ((size_t)img * g.Cout + co) * g.Ho * g.Wo;
+    }
+    const auto ry = make_rsrc(y, (size_t)g.N * g.Cout * g.Ho * g.Wo * ES);
+    const int hw = g.Ho * g.Wo;
 #pragma unroll
-    for (int a = 0; a < M; ++a) {
-        const int h = ty * M + a;
-        if (h >= g.Ho) break;
+    for (int rb = 0; rb < RB; ++rb) {
+        h8 ka[2][2];
+        const int row = 16 * rb + nl;
 #pragma unroll
-        for (int b = 0; b < M; ++b) {
-            float o = 0.0f;
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int j = 0; j < N; ++j)
-                if ((AMASK >> (b * N + j)) & 1) o = __builtin_fmaf(z[a][j], mt.At[b * N + j], o);
-            const int w = tx * M + b;
-            if (w < g.Wo) store_act(yp + (size_t)h * g.Wo + w, o * sy);
+            for (int part = 0; part < 2; ++part) ka[ks][part] = *(const h8 *)&ktab[part][swz(row, 4 * ks + kg)];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            f4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int part = 0; part < 2; ++part)
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[ks][part], bq[cb][ks], d, 0, 0, 0);
+            const int co = co0 + 4 * wave + cb;
+            if (co < g.Cout) {
+                const int soff = co * hw * ES;
+                const int o = ooff[rb], n = nv[rb];
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = d[i] * so[cb];
+                if constexpr (ES == 4) {
+                    if (n == 4) {
+                        const v4i q = {(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1]),
+                                       (int)__float_as_uint(v[2]), (int)__float_as_uint(v[3])};
+                        __builtin_amdgcn_raw_buffer_store_b128(q, ry, o, soff, 0);
+                    } else {
+                        if (n >= 2) {
+                            typedef int v2i __attribute__((ext_vector_type(2)));
+                            const v2i q = {(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1])};
+                            __builtin_amdgcn_raw_buffer_store_b64(q, ry, o, soff, 0);
+                        }
+                        if (n & 1) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[n - 1]), ry, o + 4 * (n - 1), soff, 0);
+                    }
+                } else {
+                    uint32_t hb[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t u = __float_as_uint(v[i]);
+                        hb[i] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+                    }
+                    if (n == 4) {
+                        typedef int v2i __attribute__((ext_vector_type(2)));
+                        const v2i q = {(int)(hb[0] | hb[1] << 16), (int)(hb[2] | hb[3] << 16)};
+                        __builtin_amdgcn_raw_buffer_store_b64(q, ry, o, soff, 0);
+                    } else {
+                        if (n >= 2) __builtin_amdgcn_raw_buffer_store_b32(hb[0] | hb[1] << 16, ry, o, soff, 0);
+                        if (n & 1) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hb[n - 1], ry, o + 2 * (n - 1), soff, 0);
+                    }
+                }
+            }
         }
     }
 }
@@ -999,14 +1137,11 @@ static void stage3_m(const Geo &g, const Mats &mt, const float *Mi, YT *y, int8_
 template <int M, int G, typename YT>
 static void fused_m_g(const Geo &g, const Mats &mt, const int8_t *Vq, const float *sV,
                       const int8_t *Uq, const float *sU, YT *y, hipStream_t s) {
-    constexpr uint64_t pat = M == 4 ? kAtPattern4 : kAtPattern6;
     const unsigned blocks = (unsigned)(((g.T + 15) / 16) * ((g.Cout + 15) / 16));
-    if (g.at_std)
-        hipLaunchKernelGGL((k_fused23<M, G, pat, YT>), dim3(blocks), dim3(256), 0, s, Vq, sV, Uq, sU, y,
-                           mt, g);
+    if (g.ng == 1)
+        hipLaunchKernelGGL((k_fused23<M, G, 1, YT>), dim3(blocks), dim3(256), 0, s, Vq, sV, Uq, sU, y, mt, g);
     else
-        hipLaunchKernelGGL((k_fused23<M, G, ~0ull, YT>), dim3(blocks), dim3(256), 0, s, Vq, sV, Uq, sU,
-                           y, mt, g);
+        hipLaunchKernelGGL((k_fused23<M, G, 4, YT>), dim3(blocks), dim3(256), 0, s, Vq, sV, Uq, sU, y, mt, g);
 }
 
 template <int M, typename YT>

@@ -388,6 +388,22 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
     for (int i = 0; i < n * 3; ++i)
         if (!isfinite(mt.G[i])) return fail(WQ8_ERR_INVALID_ARG, "G overflows fp32");
 
+    // power-of-two prescale of the output transform's Kronecker matrix
+    // (A^T (x) A^T, formed on the GPU in fp16 parts): largest entry <= 2^14
+    {
+        float amax = 0.0f;
+        for (int i = 0; i < m * n; ++i) amax = fmaxf(amax, fabsf(mt.At[i]));
+        int e = 0;
+        if (amax > 0.0f) {
+            frexp((double)amax * (double)amax, &e);  // amax^2 < 2^e
+            e -= 14;
+        }
+        mt.kscale = (float)ldexp(1.0, -e);
+        mt.oscale = (float)ldexp(1.0, e);
+        if (mt.kscale == 0.0f || !isfinite(mt.kscale) || !isfinite(mt.oscale))
+            return fail(WQ8_ERR_UNSUPPORTED, "A^T entries span more than fp32 allows");
+    }
+
     // may the kernels skip the structurally zero terms of the standard points?
     {
         uint64_t bt_nz = 0, at_nz = 0;
