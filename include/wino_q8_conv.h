@@ -28,8 +28,9 @@
  *   y  = sY * (A^T Yq A), cropped to Ho x Wo:  y [N][Cout][Ho][Wo]
  * Quantizer: a = max|v| over the group; a == 0 -> codes 0, scale 0; otherwise
  * code = clamp(rint(v * (127/a)), -127, 127) (ties to even), scale = a/127.
- * All transform sums are fp32 fma chains in index order, so results are
- * reproducible bit for bit.
+ * All transform sums up to the Y codes are fp32 fma chains in index order,
+ * so codes and scales are reproducible bit for bit (see wq8_algo for the
+ * output transform).
  *
  * Convolution semantics: 3x3 cross-correlation, stride 1, zero padding `pad`
  * (0..2), no bias, NCHW activations.
@@ -70,11 +71,17 @@ typedef enum {
 
 typedef enum { WQ8_F32 = 0, WQ8_BF16 = 1 } wq8_dtype;
 
-/* How wq8_conv_forward runs stages 2 and 3 (same results either way):
+/* How wq8_conv_forward runs stages 2 and 3. Both give bit-identical M, Y
+ * scales and Y codes; they differ only in how A^T Yq A is evaluated:
  *   STAGED: an int8 GEMM kernel writes M (fp32) to the workspace and a second
- *           kernel requantizes it and applies the output transform;
+ *           kernel requantizes it and applies the output transform as fp32
+ *           fma chains in index order (bit-identical to that definition);
  *   FUSED:  one kernel keeps M on chip (LDS/registers) per 16 tiles x 16
- *           output channels, re-reading the prepared weights per tile block;
+ *           output channels, re-reading the prepared weights per tile block,
+ *           and evaluates vec(O) = (A^T kron A^T) vec(Yq) on fp16 matrix
+ *           cores with the Kronecker matrix split into two fp16 parts
+ *           (fp32 accumulation): outputs within ~1e-5 of their RMS of the
+ *           fp32 evaluation;
  *   AUTO:   FUSED when the weights are small enough that re-reading them
  *           costs less than writing and reading M, else STAGED. */
 typedef enum { WQ8_ALGO_AUTO = 0, WQ8_ALGO_STAGED = 1, WQ8_ALGO_FUSED = 2 } wq8_algo;
@@ -142,8 +149,8 @@ wq8_status wq8_stage2_i32(const wq8_plan *plan, const int8_t *Vq, const int8_t *
 wq8_status wq8_stage3(const wq8_plan *plan, const float *M, void *y, int8_t *Yq,
                       float *sY, void *stream);
 
-/* Stages 2 and 3 as the single fused kernel (M stays on chip): the same y as
- * wq8_stage2 followed by wq8_stage3. */
+/* Stages 2 and 3 as the single fused kernel (M stays on chip): the same Y
+ * codes as wq8_stage2 followed by wq8_stage3; y as described for FUSED. */
 wq8_status wq8_stage23(const wq8_plan *plan, const int8_t *Vq, const float *sV,
                        const int8_t *Uq, const float *sU, void *y, void *stream);
 

@@ -248,3 +248,25 @@ def test_full_size_sampled(dev, L, algo):
     err = float(np.max(np.abs(got.astype(np.float64) - want)))
     assert err <= OUT_TOL * rms(want), f"max err {err:.3e} rms {rms(want):.3e}"
     print(f"[case] full {L.name} ({algo}): sampled max err {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["c2_f6_n32_c64_56x56_g64", "c4_f4_n2_c320_64x64_g64_pert",
+                                  "c5_f6_n8_c640_32x32_g32"])
+def test_fused_output_transform_precision(dev, name):
+    """The fused kernel evaluates A^T Yq A on fp16 matrix cores with the
+    Kronecker matrix split into two fp16 parts; on identical codes it must
+    agree with the staged fp32 chain to a few 1e-6 of the output RMS (far
+    inside the 1e-3 output tolerance)."""
+    L = WL.small(WL.LAYERS[name], N=2, H=23, W=21, Cin=64, Cout=48)
+    print(f"\n[case] fused-vs-staged precision {L.name}", flush=True)
+    d = WL.make(L)
+    ys = {}
+    for algo in ("staged", "fused"):
+        plan = make_plan(L, d, algo=algo)
+        Uq, sU = q.wq8_weights_prepare(plan, to_dev(d["w"], dev))
+        ys[algo] = q.wq8_conv_forward(plan, to_dev(d["x"], dev), Uq, sU).cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    err = float(np.max(np.abs(ys["fused"] - ys["staged"])))
+    r = rms(ys["staged"])
+    print(f"[case] max |fused - staged| = {err:.3e} = {err / r:.2e} rms", flush=True)
+    assert err <= 2e-5 * r
