@@ -28,6 +28,7 @@ struct Geo {
                               // points' matrices do (zero terms may be skipped)
     int co_major;             // fused kernel: 1 = output-channel blocks outermost
                               // (weights larger than the activation codes)
+    int fused_waves;          // fused kernel: waves per block (4 or 16)
 };
 
 // Nonzero patterns of B^T [n][n] and A^T [m][n] for the standard points

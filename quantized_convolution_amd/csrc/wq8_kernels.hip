@@ -690,46 +690,91 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
 // block on int8 MFMA with U as the A operand (rows = output channels) and V as
 // the B operand (columns = tiles), so lane (r, kq) ends with the four
 // (co = 4kq + i, t = r) pairs for its taps. The per-group dequantization is
-// the same fma chain over groups as stage 2, so M is bit-identical to it.
+// the same fma chain over groups as stage 2, so M is bit-identical to it. The
+// group scales of a wave's taps are staged in LDS, one group at a time, the
+// next group's loaded while the current one is computed.
 //
 // Y: the absmax of a pair over all taps combines the four waves' partial
 // maxima through LDS; one thread per pair computes 127/a and a/127 (the same
 // IEEE divisions as stage 3) and the codes are rounded by the wave that holds
-// the values. Codes are small integers, exact in fp16, and go to LDS as fp16.
+// the values, then stored in LDS as bytes biased by +128.
 //
 // Output transform: for each pair, vec(O) = (A^T (x) A^T) vec(Yq), one dense
-// [m*m] x [n*n] product for all 256 pairs of the block, on fp16 MFMA
-// (16x16x32, fp32 accumulation). The Kronecker matrix K (built per block in
-// LDS from A^T) is scaled by a power of two and split into fp16 high and low
-// parts, K = Kh + Kl, so Kh*Yq + Kl*Yq carries about 22 significant bits of
-// K: the result differs from an fp32 evaluation of A^T Yq A by ~1e-6 of its
-// RMS, well inside the tolerance of the output (which, unlike the codes, is
-// not required to be bit-exact).
+// product for all 256 pairs of the block on fp16 MFMA (16x16x32, fp32
+// accumulation). Codes are exact in fp16. The Kronecker matrix K (built per
+// block in LDS from A^T) is scaled by a power of two and split into fp16 high
+// and low parts, K = Kh + Kl, so Kh*Yq + Kl*Yq carries about 22 significant
+// bits of K: the result differs from an fp32 evaluation of A^T Yq A by ~1e-6
+// of its RMS, well inside the tolerance of the output (which, unlike the
+// codes, is not required to be bit-exact). Product rows are (a, b) with b
+// padded to BS, so a lane's four rows are adjacent pixels of one output row.
 //
-// LDS rows of 64 fp16 (one pair's codes, or one row of K) are 128 bytes; the
-// 16-byte chunk c of row p is stored at chunk c ^ ((p >> 1) & 7), which makes
-// the 16-lane 16-byte reads and writes below free of bank conflicts.
-__device__ __forceinline__ int swz(int row, int chunk) { return (row << 6) + ((chunk ^ ((row >> 1) & 7)) << 3); }
+// LDS stays below 40 KB and registers below 128 so that four blocks share a
+// CU: on the ResNet-18 layer all 800 blocks then run in a single wave of
+// residency instead of 768 plus a tail of 32.
+constexpr int kCodeBias = 128;
+constexpr float kBiasedMagic = 12583040.0f;  // 1.5 * 2^23 + 128 (even)
+
+// Code rows: 64 bytes per pair; 8-byte chunk c of pair p at c ^ ((p >> 2) & 7).
+__device__ __forceinline__ int cswz(int p, int c) { return (p << 6) + ((c ^ ((p >> 2) & 7)) << 3); }
+// K rows: 64 fp16 per row; 16-byte chunk c of row q at c ^ ((q >> 1) & 7).
+__device__ __forceinline__ int kswz(int q, int c) { return (q << 6) + ((c ^ ((q >> 1) & 7)) << 3); }
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
-template <int M, int G, int GC, typename YT>
-__global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
+// Four biased codes (low byte of each float's bits) -> one dword, byte k = x[k].
+__device__ __forceinline__ uint32_t pack4(float x0, float x1, float x2, float x3) {
+    const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(x3), __float_as_uint(x2), 0x04000c0cu);
+    return lo | hi;
+}
+
+// Eight biased code bytes -> eight fp16 codes: bytes u become fp16 bit
+// patterns 0x6400 | u = 1024 + u, and 1024 + u - 1152 = u - 128 exactly.
+__device__ __forceinline__ h8 unbias8(v2i w) {
+    h8 r;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t x = (uint32_t)w[k];
+        const uint32_t p0 = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);
+        const uint32_t p1 = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
+        const h2 q0 = __builtin_bit_cast(h2, p0) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
+        const h2 q1 = __builtin_bit_cast(h2, p1) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
+        r[4 * k + 0] = q0[0];
+        r[4 * k + 1] = q0[1];
+        r[4 * k + 2] = q1[0];
+        r[4 * k + 3] = q1[1];
+    }
+    return r;
+}
+
+// WPB: waves per block (the block's taps are split evenly between them).
+// MULTI: more than one quantization group along Cin (the group loop runs and
+// prefetches across groups).
+template <int M, int G, int WPB, bool MULTI, typename YT>
+__global__ __launch_bounds__(64 * WPB, WPB == 4 && MULTI ? 3 : 4) void k_fused23(const int8_t *__restrict__ Vq,
                                                  const float *__restrict__ sV,
                                                  const int8_t *__restrict__ Uq,
                                                  const float *__restrict__ sU, YT *__restrict__ y,
                                                  Mats mt, Geo g) {
-    constexpr int N = M + 2, NT = N * N, TPW = NT / 4;
+    constexpr int N = M + 2, NT = N * N, TPW = NT / WPB, MM = M * M, NTH = 64 * WPB;
+    constexpr int CBW = 16 / WPB;       // output column blocks (16 pairs) per wave
     constexpr int BS = M == 6 ? 8 : 4;  // output row a, column b -> product row a * BS + b
-    constexpr int MR = M * BS, RB = MR / 16;  // rows and 16-row blocks of the output product
+    constexpr int RB = M * BS / 16;     // 16-row blocks of the output product
     constexpr bool K64 = G % 64 == 0;
     constexpr int KSTEPS = K64 ? G / 64 : 1;
     constexpr int ES = sizeof(YT);
-    static_assert(NT <= 64 && TPW * 4 == NT && TPW <= 16, "taps per wave");
-    __shared__ __attribute__((aligned(16))) _Float16 codes[256 * 64];
-    __shared__ __attribute__((aligned(16))) _Float16 ktab[2][MR * 64];
-    __shared__ float pmax[4][256];
+    static_assert(NT <= 64 && TPW * WPB == NT && TPW <= 16 && CBW * WPB == 16, "taps per wave");
+    // codes: 256 pairs x 64 bytes; during the Hadamard part each wave uses its
+    // share (16 KB / WPB) for one group's scales [2][TPW taps][16 rows], then
+    // for its partial maxima (256 floats)
+    constexpr int WLDS = 4096 / WPB;  // floats per wave
+    static_assert(WLDS >= 256 && WLDS >= 2 * TPW * 16, "per-wave LDS share");
+    __shared__ __attribute__((aligned(16))) uint8_t codes[256 * 64];
+    __shared__ __attribute__((aligned(16))) _Float16 ktab[2][MM * 64];  // K rows a * m + b
     __shared__ float s_inv[256], s_out[256];
     __shared__ float at_lds[M * N];
 
@@ -745,7 +790,30 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
     const int t0 = tb * 16, co0 = cob * 16;
     const int tap0 = wave * TPW;
     const size_t vplane = (size_t)g.T * g.Cin, uplane = (size_t)g.Cout * g.Cin;
+    float *wlds = reinterpret_cast<float *>(codes) + wave * WLDS;
+
+    // ---- K = A^T (x) A^T (rows a * m + b, taps i * n + j), scaled, fp16 hi/lo
     if (tid < M * N) at_lds[tid] = mt.At[tid];
+    __syncthreads();
+    for (int task = tid; task < MM * 8; task += NTH) {
+        const int q = task >> 3, c = task & 7;
+        const int a = q / M, b = q % M;
+        h8 hi, lo;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int tap = 8 * c + u;
+            float kv = 0.0f;
+            if (tap < NT) {
+                const int i = tap / N, j = tap - (tap / N) * N;
+                kv = (at_lds[a * N + i] * mt.kscale) * at_lds[b * N + j];
+            }
+            const _Float16 h = (_Float16)kv;
+            hi[u] = h;
+            lo[u] = (_Float16)(kv - (float)h);
+        }
+        *(h8 *)&ktab[0][kswz(q, c)] = hi;
+        *(h8 *)&ktab[1][kswz(q, c)] = lo;
+    }
 
     // ---- Hadamard GEMMs for this wave's taps
     // Rows past T or Cout read row 0 instead: they only feed (tile, co) pairs
@@ -770,9 +838,10 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[j][i] = 0.0f;
 
-    // Operands of one tap for one group.
+    // Operands of one tap for one group (G < 64: one 8-byte K slice each).
     struct TapOps {
-        v4i a[K64 ? KSTEPS : 1], b[K64 ? KSTEPS : 1];
+        v4i a[K64 ? KSTEPS : 0], b[K64 ? KSTEPS : 0];
+        long a8, b8;
     };
     auto load_tap = [&](int j, int gi, TapOps &o) {
         const int tap = tap0 + j;
@@ -786,41 +855,39 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
         } else {
             const auto a2 = __builtin_amdgcn_raw_buffer_load_b64(rU, uoff, us, 0);
             const auto b2 = __builtin_amdgcn_raw_buffer_load_b64(rV, voff, vs, 0);
-            o.a[0] = v4i{(int)a2[0], (int)a2[1], 0, 0};
-            o.b[0] = v4i{(int)b2[0], (int)b2[1], 0, 0};
+            o.a8 = ((long)(uint32_t)a2[1] << 32) | (uint32_t)a2[0];
+            o.b8 = ((long)(uint32_t)b2[1] << 32) | (uint32_t)b2[0];
         }
     };
-    // Group scales of this wave's taps for GC groups at a time, staged in LDS
-    // (in the code area, idle until the Hadamard part ends) with a few wide
-    // loads: sv[j][gg][tile row], su[j][gg][channel row]; 8 KB per wave.
-    float *scl = reinterpret_cast<float *>(codes) + wave * (2 * 16 * GC * 16);
-    auto stage_scales = [&](int g0) {
-        // lane slot e = 64k + lane: k < 4 -> sv, else su; tap j = (e / 16) % 16; row = lane % 16
-        float sreg[8][GC];
+    // Group scales of this wave's taps for one group, staged in its LDS
+    // quarter: wlds[(s * 16 + j) * 16 + row], s = 0 for sV (row = tile), 1 for
+    // sU (row = output channel). The next group's are loaded into registers
+    // while the current group is computed.
+    // slot e = 64k + lane: s = e / (16 TPW) (0: sV, row = tile; 1: sU, row =
+    // output channel), tap j = (e / 16) % TPW, row = e % 16
+    constexpr int SL = (2 * TPW * 16 + 63) / 64;  // scale loads per lane
+    auto load_scales = [&](int gi, float (&sreg)[SL]) {
         const int row = lane & 15;
         const int tr = t0 + row < g.T ? t0 + row : 0, cr = co0 + row < g.Cout ? co0 + row : 0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int j = (4 * k + (lane >> 4)) & 15;
-            const int tap = tap0 + (j < TPW ? j : 0);
-            const auto rs = k < 4 ? rsV : rsU;
-            const int off = k < 4 ? ((tap * (int)g.T + tr) * g.ng + g0) * 4 : ((tap * g.Cout + cr) * g.ng + g0) * 4;
-            if constexpr (GC == 4) {
-                const v4i q = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) sreg[k][u] = __int_as_float(q[u]);
-            } else {
-                sreg[k][0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int j = (4 * k + (lane >> 4)) & 15;
-#pragma unroll
-            for (int u = 0; u < GC; ++u) scl[(((k >> 2) * 16 + j) * GC + u) * 16 + row] = sreg[k][u];
+        for (int k = 0; k < SL; ++k) {
+            const int e = 64 * k + lane;
+            const int sw = e / (16 * TPW), j = (e / 16) % TPW;
+            const int tap = tap0 + j;
+            const int off = sw == 0 ? ((tap * (int)g.T + tr) * g.ng + gi) * 4 : ((tap * g.Cout + cr) * g.ng + gi) * 4;
+            // slots past 2 * TPW * 16 (sw == 2) read past the end: zero, never stored
+            sreg[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sw == 0 ? rsV : rsU,
+                                                                           sw < 2 ? off : 0x7ffffff0, 0, 0));
         }
     };
-    auto use_tap = [&](int j, int gg, const TapOps &o) {
+    auto put_scales = [&](const float (&sreg)[SL]) {
+#pragma unroll
+        for (int k = 0; k < SL; ++k) {
+            const int e = 64 * k + lane;
+            if (e < 2 * TPW * 16) wlds[e] = sreg[k];
+        }
+    };
+    auto use_tap = [&](int j, const TapOps &o) {
         v4i P = v4i{0, 0, 0, 0};
         if constexpr (K64) {
 #pragma unroll
@@ -828,14 +895,10 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
                 P = __builtin_amdgcn_mfma_i32_16x16x64_i8(o.a[ks], o.b[ks], P, 0, 0, 0);
         } else {
             // K = 32; for G = 16 the upper 16 K slots are zero
-            long a = ((long)(uint32_t)o.a[0][1] << 32) | (uint32_t)o.a[0][0];
-            long b = ((long)(uint32_t)o.b[0][1] << 32) | (uint32_t)o.b[0][0];
-            a = kin ? a : 0;
-            b = kin ? b : 0;
-            P = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, P, 0, 0, 0);
+            P = __builtin_amdgcn_mfma_i32_16x16x32_i8(kin ? o.a8 : 0, kin ? o.b8 : 0, P, 0, 0, 0);
         }
-        const float sv = scl[(j * GC + gg) * 16 + r];
-        const float4 su = *(const float4 *)&scl[((16 + j) * GC + gg) * 16 + 4 * kq];
+        const float sv = wlds[j * 16 + r];
+        const float4 su = *(const float4 *)&wlds[(TPW + j) * 16 + 4 * kq];
         const float sus[4] = {su.x, su.y, su.z, su.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -843,43 +906,63 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
             acc[j][i] = __builtin_fmaf(sc, (float)P[i], acc[j][i]);
         }
     };
-    // two batches of taps in flight: the next batch's loads are issued before
-    // the current batch's MFMAs and dequantization
-    constexpr int BATCH = KSTEPS >= 4 ? 1 : KSTEPS == 2 ? (TPW % 2 == 0 ? 2 : 3)
-                                                        : (TPW % 4 == 0 ? 4 : 3);
-    for (int g0 = 0; g0 < g.ng; g0 += GC) {
-        stage_scales(g0);
-        const int gend = g0 + GC < g.ng ? g0 + GC : g.ng;
-        for (int gi = g0; gi < gend; ++gi) {
-            TapOps buf[2][BATCH];
+    // Two batches of taps in flight: the next batch's loads (of this group or,
+    // when a group has an even number of batches, of the next group) are
+    // issued before the current batch's MFMAs and dequantization.
+    constexpr int BATCH = KSTEPS >= 2 ? 1
+                          : TPW % 4 == 0 && TPW / 4 % 2 == 0 && !K64 ? 4
+                          : TPW % 2 == 0 ? 2 : TPW % 3 == 0 ? 3 : 1;
+    constexpr int NB = TPW / BATCH;
+    constexpr bool XG = NB % 2 == 0;  // prefetch across group boundaries
+    static_assert(NB * BATCH == TPW, "batches per group");
+    TapOps buf[2][BATCH];
+    float snext[SL];
+    load_scales(0, snext);
+    if constexpr (XG) {
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) load_tap(b, 0, buf[0][b]);
+    }
+    const int ng = MULTI ? g.ng : 1;
+    for (int gi = 0; gi < ng; ++gi) {
+        put_scales(snext);
+        const int gnext = gi + 1 < ng ? gi + 1 : gi;  // the last group reloads itself (unused)
+        load_scales(gnext, snext);
+        if constexpr (!XG) {
 #pragma unroll
             for (int b = 0; b < BATCH; ++b) load_tap(b, gi, buf[0][b]);
+        }
 #pragma unroll
-            for (int jb = 0; jb < TPW; jb += BATCH) {
-                const int cur = (jb / BATCH) & 1;
-                if (jb + BATCH < TPW)
+        for (int jb = 0; jb < TPW; jb += BATCH) {
+            const int cur = (jb / BATCH) & 1;
+            if (jb + BATCH < TPW) {
 #pragma unroll
-                    for (int b = 0; b < BATCH; ++b) load_tap(jb + BATCH + b, gi, buf[cur ^ 1][b]);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int b = 0; b < BATCH; ++b) load_tap(jb + BATCH + b, gi, buf[cur ^ 1][b]);
+            } else if (XG) {
 #pragma unroll
-                for (int b = 0; b < BATCH; ++b) use_tap(jb + b, gi - g0, buf[cur][b]);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int b = 0; b < BATCH; ++b) load_tap(b, gnext, buf[cur ^ 1][b]);
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) use_tap(jb + b, buf[cur][b]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // ---- Y absmax per pair: partial maxima of this wave's taps
+    // ---- Y absmax per pair: partial maxima of this wave's taps (its own LDS
+    // quarter is free once its Hadamard part is done)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float m = 0.0f;
 #pragma unroll
         for (int j = 0; j < TPW; ++j) m = fmaxf(m, fabsf(acc[j][i]));
-        pmax[wave][(4 * kq + i) * 16 + r] = m;
+        wlds[(4 * kq + i) * 16 + r] = m;
     }
     __syncthreads();
-    {
-        // one thread per pair: the scales. K in LDS: row ab, 8 taps per task.
-        const float am = fmaxf(fmaxf(pmax[0][tid], pmax[1][tid]), fmaxf(pmax[2][tid], pmax[3][tid]));
+    if (tid < 256) {
+        const float *pm = reinterpret_cast<const float *>(codes);
+        float am = pm[tid];
+#pragma unroll
+        for (int w = 1; w < WPB; ++w) am = fmaxf(am, pm[w * WLDS + tid]);
         float inv = 0.0f, sy = 0.0f;
         if (am != 0.0f) {
             inv = 127.0f / am;
@@ -887,66 +970,50 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
         }
         s_inv[tid] = inv;
         s_out[tid] = sy * mt.oscale;
-        for (int task = tid; task < MR * 8; task += 256) {
-            const int row = task >> 3, c = task & 7;
-            const int a = row / BS, b = row % BS;
-            h8 hi, lo;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int tap = 8 * c + u;
-                float kv = 0.0f;
-                if (tap < NT && b < M) {
-                    const int i = tap / N, j = tap - (tap / N) * N;
-                    kv = (at_lds[a * N + i] * mt.kscale) * at_lds[b * N + j];
-                }
-                const _Float16 h = (_Float16)kv;
-                hi[u] = h;
-                lo[u] = (_Float16)(kv - (float)h);
-            }
-            *(h8 *)&ktab[0][swz(row, c)] = hi;
-            *(h8 *)&ktab[1][swz(row, c)] = lo;
-        }
     }
     __syncthreads();
-    // ---- codes of this wave's taps, fp16, into the pair rows
+    // ---- codes of this wave's taps, biased bytes, into the pair rows
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int p = (4 * kq + i) * 16 + r;
         const float inv = s_inv[p];
+        float yb[TPW];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) yb[j] = acc[j][i] * inv + kBiasedMagic;  // low byte: code + 128
         if constexpr (TPW % 8 == 0) {
 #pragma unroll
             for (int c = 0; c < TPW / 8; ++c) {
-                h8 q;
-#pragma unroll
-                for (int u = 0; u < 8; ++u) q[u] = (_Float16)__builtin_rintf(acc[8 * c + u][i] * inv);
-                *(h8 *)&codes[swz(p, tap0 / 8 + c)] = q;
+                const v2i w = {(int)pack4(yb[8 * c], yb[8 * c + 1], yb[8 * c + 2], yb[8 * c + 3]),
+                               (int)pack4(yb[8 * c + 4], yb[8 * c + 5], yb[8 * c + 6], yb[8 * c + 7])};
+                *(v2i *)&codes[cswz(p, tap0 / 8 + c)] = w;
             }
+        } else if constexpr (TPW == 4) {
+            *(uint32_t *)&codes[cswz(p, tap0 >> 3) + (tap0 & 7)] = pack4(yb[0], yb[1], yb[2], yb[3]);
         } else {
 #pragma unroll
             for (int j = 0; j < TPW; ++j) {
                 const int tap = tap0 + j;
-                codes[swz(p, tap >> 3) + (tap & 7)] = (_Float16)__builtin_rintf(acc[j][i] * inv);
+                codes[cswz(p, tap >> 3) + (tap & 7)] = (uint8_t)__float_as_uint(yb[j]);
             }
         }
     }
-    if constexpr (NT < 64) {
-        // taps NT..63 of every pair row: zero (K is zero there; keep B finite)
-        for (int tap = NT; tap < 64; ++tap) codes[swz(tid, tap >> 3) + (tap & 7)] = (_Float16)0.0f;
-    }
     __syncthreads();
 
-    // ---- output transform: D[ab][pair] = sum_tap K[ab][tap] * Yq[tap][pair]
-    // Wave w takes pairs 64w .. 64w+63 (4 column blocks of 16 = tiles t0..t0+15
-    // of output channel co0 + 4w + cb). Lane (kg = lane / 16, nl = lane % 16).
+    // ---- output transform: D[row][pair] = sum_tap K[row][tap] * Yq[tap][pair]
+    // Column block cb (pairs 16cb .. 16cb+15 = tiles t0..t0+15 of output
+    // channel co0 + cb) goes to wave cb % WPB. Lane (kg = lane / 16, nl = lane % 16).
+    // Taps NT..63 of a code row hold stale bytes: finite codes, multiplied by
+    // K = 0 there.
     const int kg = lane >> 4, nl = lane & 15;
-    h8 bq[4][2];
+    h8 bq[CBW][2];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int c = 0; c < CBW; ++c)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) bq[cb][ks] = *(const h8 *)&codes[swz(64 * wave + 16 * cb + nl, 4 * ks + kg)];
-    float so[4];
+        for (int ks = 0; ks < 2; ++ks)
+            bq[c][ks] = unbias8(*(const v2i *)&codes[cswz(16 * (wave + WPB * c) + nl, 4 * ks + kg)]);
+    float so[CBW];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) so[cb] = s_out[64 * wave + 16 * cb + nl];
+    for (int c = 0; c < CBW; ++c) so[c] = s_out[16 * (wave + WPB * c) + nl];
 
     // This lane's tile; per row block, the output pixel (a, b0) of its first
     // row 16rb + 4kg and how many of its 4 adjacent pixels b0..b0+3 are inside
@@ -970,21 +1037,25 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
     const int hw = g.Ho * g.Wo;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+        // A fragment: product row 16rb + nl = (a, b); padding rows are zero
         h8 ka[2][2];
-        const int row = 16 * rb + nl;
+        const int prow = 16 * rb + nl, pa = prow / BS, pb = prow % BS;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int part = 0; part < 2; ++part) ka[ks][part] = *(const h8 *)&ktab[part][swz(row, 4 * ks + kg)];
+            for (int part = 0; part < 2; ++part) {
+                if (pb < M) ka[ks][part] = *(const h8 *)&ktab[part][kswz(pa * M + pb, 4 * ks + kg)];
+                else ka[ks][part] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+            }
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
+        for (int cb = 0; cb < CBW; ++cb) {
             f4 d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int part = 0; part < 2; ++part)
                     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[ks][part], bq[cb][ks], d, 0, 0, 0);
-            const int co = co0 + 4 * wave + cb;
+            const int co = co0 + wave + WPB * cb;
             if (co < g.Cout) {
                 const int soff = co * hw * ES;
                 const int o = ooff[rb], n = nv[rb];
@@ -998,7 +1069,6 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
                         __builtin_amdgcn_raw_buffer_store_b128(q, ry, o, soff, 0);
                     } else {
                         if (n >= 2) {
-                            typedef int v2i __attribute__((ext_vector_type(2)));
                             const v2i q = {(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1])};
                             __builtin_amdgcn_raw_buffer_store_b64(q, ry, o, soff, 0);
                         }
@@ -1012,7 +1082,6 @@ __global__ __launch_bounds__(256) void k_fused23(const int8_t *__restrict__ Vq,
                         hb[i] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
                     }
                     if (n == 4) {
-                        typedef int v2i __attribute__((ext_vector_type(2)));
                         const v2i q = {(int)(hb[0] | hb[1] << 16), (int)(hb[2] | hb[3] << 16)};
                         __builtin_amdgcn_raw_buffer_store_b64(q, ry, o, soff, 0);
                     } else {
@@ -1138,10 +1207,23 @@ template <int M, int G, typename YT>
 static void fused_m_g(const Geo &g, const Mats &mt, const int8_t *Vq, const float *sV,
                       const int8_t *Uq, const float *sU, YT *y, hipStream_t s) {
     const unsigned blocks = (unsigned)(((g.T + 15) / 16) * ((g.Cout + 15) / 16));
-    if (g.ng == 1)
-        hipLaunchKernelGGL((k_fused23<M, G, 1, YT>), dim3(blocks), dim3(256), 0, s, Vq, sV, Uq, sU, y, mt, g);
-    else
-        hipLaunchKernelGGL((k_fused23<M, G, 4, YT>), dim3(blocks), dim3(256), 0, s, Vq, sV, Uq, sU, y, mt, g);
+    // 16 waves per block when 4-wave blocks would leave most wave slots idle
+    // (few tiles, many channels): more loads in flight per CU
+    if constexpr (M == 6) {
+        if (g.fused_waves == 16) {
+            if (g.ng == 1)
+                hipLaunchKernelGGL((k_fused23<M, G, 16, false, YT>), dim3(blocks), dim3(1024), 0, s, Vq, sV, Uq, sU, y, mt, g);
+            else
+                hipLaunchKernelGGL((k_fused23<M, G, 16, true, YT>), dim3(blocks), dim3(1024), 0, s, Vq, sV, Uq, sU, y, mt, g);
+            return;
+        }
+    }
+    {
+        if (g.ng == 1)
+            hipLaunchKernelGGL((k_fused23<M, G, 4, false, YT>), dim3(blocks), dim3(256), 0, s, Vq, sV, Uq, sU, y, mt, g);
+        else
+            hipLaunchKernelGGL((k_fused23<M, G, 4, true, YT>), dim3(blocks), dim3(256), 0, s, Vq, sV, Uq, sU, y, mt, g);
+    }
 }
 
 template <int M, typename YT>

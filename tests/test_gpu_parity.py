@@ -270,3 +270,27 @@ def test_fused_output_transform_precision(dev, name):
     r = rms(ys["staged"])
     print(f"[case] max |fused - staged| = {err:.3e} = {err / r:.2e} rms", flush=True)
     assert err <= 2e-5 * r
+
+
+@pytest.mark.parametrize("waves", [4, 16])
+@pytest.mark.parametrize("name,kw", [
+    ("c2_f6_n32_c64_56x56_g64", dict(N=2, H=30, W=26, Cin=64, Cout=40)),
+    ("c3c_f6_n32_c512_7x7_g64", dict(N=3, H=7, W=7, Cin=192, Cout=24)),
+    ("c5_f6_n8_c640_32x32_g32", dict(N=1, H=13, W=17, Cin=96, Cout=20)),
+    ("c5_f6_n8_c1280_16x16_g128", dict(N=1, H=9, W=11, Cin=256, Cout=17)),
+])
+def test_fused_block_shapes(dev, monkeypatch, waves, name, kw):
+    """The fused kernel splits a block's taps over 4 or 16 waves (the plan
+    picks by block count; WQ8_FUSED_WAVES forces one): both shapes give the
+    oracle's result, for one and several quantization groups."""
+    monkeypatch.setenv("WQ8_FUSED_WAVES", str(waves))
+    L = WL.small(WL.LAYERS[name], **kw)
+    print(f"\n[case] fused waves={waves} {L.name} C={L.Cin}->{L.Cout} {L.H}x{L.W} G={L.G}", flush=True)
+    d = WL.make(L)
+    ref = oracle.forward(L.m, d["x"], d["w"], L.pad, L.G, points=list(d["points"]), s_b=d["s_b"],
+                         s_g=d["s_g"])
+    plan = make_plan(L, d, algo="fused")
+    Uq, sU = q.wq8_weights_prepare(plan, to_dev(d["w"], dev))
+    y = q.wq8_conv_forward(plan, to_dev(d["x"], dev), Uq, sU)
+    torch.cuda.synchronize()
+    assert_out(y.cpu().numpy(), ref, f"fused forward, {waves} waves")
