@@ -144,29 +144,62 @@ def time_events(fn, iters, stream):
     return start.elapsed_time(end) / iters  # ms
 
 
+def time_each(fn, iters, stream, before=None):
+    """Per-call times (ms) from an event pair around each call; `before` runs
+    between the calls, outside the timed pairs."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for a, b in evs:
+        if before is not None:
+            before()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
 def cpu_baseline(L, d, min_seconds=10.0):
     """The plain CPU oracle (as it stands) on the host cores, over the full
-    workload, repeated until about `min_seconds` of CPU work."""
+    workload (fp32 quantized pipeline, weight transform excluded like on the
+    GPU), repeated until about `min_seconds` of CPU work; then one run on a
+    single thread, and the fp64 direct convolution (the accuracy reference,
+    timed separately; it is not the competitor)."""
     import oracle
     from oracle import transforms as T
 
     Bt, Gm, At = T.transforms_f32(L.m, list(d["points"]), d["s_b"], d["s_g"])
     Uq, sU = oracle.weights(L.m, d["w"], L.G, Gm)
-    times = []
-    t_end = time.perf_counter() + min_seconds
-    while len(times) < 3 or time.perf_counter() < t_end:
+
+    def fwd():
         t0 = time.perf_counter()
         Vq, sV = oracle.stage1(L.m, d["x"], L.pad, L.G, Bt)
         M = oracle.stage2(Vq, sV, Uq, sU, L.G)
         oracle.stage3(L.m, M, L.N, L.H, L.W, L.pad, At)
-        times.append(time.perf_counter() - t0)
+        return time.perf_counter() - t0
+
+    cores = oracle.num_threads()
+    times = []
+    t_end = time.perf_counter() + min_seconds
+    while len(times) < 3 or time.perf_counter() < t_end:
+        times.append(fwd())
         if len(times) >= 200:
             break
     t = statistics.median(times)
+    oracle.set_num_threads(1)
+    try:
+        t1 = fwd()
+    finally:
+        oracle.set_num_threads(cores)
+    t0 = time.perf_counter()
+    oracle.direct_conv_f64(d["x"], d["w"], L.pad)
+    td = time.perf_counter() - t0
     return {"value": round(L.direct_ops() / t / 1e12, 5), "unit": "TOPS",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"full workload (N={L.N}), forward only, median of {len(times)} runs, "
-                      f"{t * 1e3:.1f} ms each"}
+            "cores": cores, "kind": "oracle",
+            "sample": f"full workload (N={L.N}), forward only (fp32 quantized pipeline), median of "
+                      f"{len(times)} runs, {t * 1e3:.1f} ms each",
+            "value_1thread": round(L.direct_ops() / t1 / 1e12, 5),
+            "direct_f64_ms": round(td * 1e3, 1)}
 
 
 def run_layer(L, algo, steps, warmup, dev):
@@ -190,6 +223,13 @@ def run_layer(L, algo, steps, warmup, dev):
     ms = time_events(step, steps, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # per-step distribution, caches warm, and cold: a 512 MiB fill before each
+    # step evicts the 256 MB Infinity Cache (and the L2s)
+    hot = time_each(step, min(steps, 100), stream)
+    flush = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+    cold = time_each(step, 20, stream, before=lambda: flush.fill_(1.0))
+    del flush
 
     # per-kernel durations: each stage entry point launches exactly the kernel
     # the forward launches, with the same grid, on the same stream
@@ -217,7 +257,8 @@ def run_layer(L, algo, steps, warmup, dev):
     dom = max(k_ms, key=k_ms.get)
     achieved = nbytes[dom] / (k_ms[dom] * 1e-3) / 1e9
     return dict(plan=plan, d=d, ms=ms, wall=wall, stages=stages, dom=dom, achieved=achieved,
-                nbytes=nbytes, tops=L.direct_ops() / (ms * 1e-3) / 1e12)
+                nbytes=nbytes, tops=L.direct_ops() / (ms * 1e-3) / 1e12,
+                hot=(statistics.median(hot), min(hot)), cold=(statistics.median(cold), min(cold)))
 
 
 def main():
@@ -276,10 +317,14 @@ def main():
                      "traffic": recorded_traffic(L.name, dom),
                      "bytes_per_launch": r["nbytes"][dom]},
         "stages": r["stages"],
+        "per_step_ms": {"median": round(r["hot"][0], 5), "min": round(r["hot"][1], 5),
+                        "cold_median": round(r["cold"][0], 5), "cold_min": round(r["cold"][1], 5),
+                        "cold_TOPS": round(L.direct_ops() / (r["cold"][0] * 1e-3) / 1e12, 3)},
         "wall_s": round(r["wall"], 3),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(L, r["d"])
+        out["cpu_baseline"]["gpu_speedup_vs_oracle"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
 
 

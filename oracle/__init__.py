@@ -44,6 +44,8 @@ def lib():
         P = C.c_void_p
         i, l = C.c_int, C.c_long
         _lib.wq8o_num_threads.restype = C.c_int
+        _lib.wq8o_set_num_threads.argtypes = [C.c_int]
+        _lib.wq8o_set_num_threads.restype = None
         _lib.wq8o_direct_conv_f64.argtypes = [i, i, i, i, i, i, P, P, P]
         _lib.wq8o_winograd_f64.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, P]
         _lib.wq8o_stage2_i32.argtypes = [i, l, i, i, i, P, P, P]
@@ -68,6 +70,11 @@ def _f32(a):
 
 def num_threads() -> int:
     return lib().wq8o_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for later calls (timing only: results are independent of it)."""
+    lib().wq8o_set_num_threads(int(n))
 
 
 def out_size(H, W, pad):

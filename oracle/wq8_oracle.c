@@ -41,6 +41,16 @@ int wq8o_num_threads(void)
 #endif
 }
 
+/* Thread count for the following calls (timing only; results do not depend on it). */
+void wq8o_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Ground truth: direct 3x3 convolution with every product and sum in fp64. */
 void wq8o_direct_conv_f64(int N, int Cin, int Cout, int H, int W, int pad,
                           const float *x, const float *w, double *y)
