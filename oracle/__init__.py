@@ -56,6 +56,9 @@ def lib():
             getattr(_lib, "wq8o_stage3" + s).argtypes = [i, i, i, i, i, i, P, P, P, P, P]
             getattr(_lib, "wq8o_sampled" + s).argtypes = [i, l, i, i, i, P, P, P, P, P, i, P, P, P,
                                                            P, P]
+            getattr(_lib, "wq8o_w8a8_quant_x" + s).argtypes = [i, i, i, i, i, P, P, P]
+            getattr(_lib, "wq8o_w8a8_quant_w" + s).argtypes = [i, i, i, P, P, P]
+            getattr(_lib, "wq8o_w8a8_conv" + s).argtypes = [i, i, i, i, i, i, i, P, P, P, P, P]
     return _lib
 
 
@@ -242,3 +245,49 @@ def sqnr_db(ref, out) -> float:
     if den == 0.0:
         return float("inf")
     return 10.0 * np.log10(num / den)
+
+
+# --------------------------------------------------------------------------
+# group-wise W8A8 direct convolution (the non-Winograd baseline)
+# --------------------------------------------------------------------------
+def direct_quant_x(x, G, prec="f32"):
+    """xq [N][H][W][Cin] int8 and sx [N][H][W][Cin/G]: per pixel, groups of G
+    consecutive input channels."""
+    x = _f32(x)
+    N, Cin, H, W = x.shape
+    assert Cin % G == 0 and G <= 256
+    rt = np.float32 if prec == "f32" else np.float64
+    xq = np.zeros((N, H, W, Cin), np.int8)
+    sx = np.zeros((N, H, W, Cin // G), rt)
+    getattr(lib(), "wq8o_w8a8_quant_x_" + prec)(N, Cin, H, W, G, _p(x), _p(xq), _p(sx))
+    return xq, sx
+
+
+def direct_quant_w(w, G, prec="f32"):
+    """wq [9][Cout][Cin] int8 and sw [9][Cout][Cin/G]: per kernel tap and
+    output channel, groups of G consecutive input channels."""
+    w = _f32(w)
+    Cout, Cin = w.shape[:2]
+    assert w.shape == (Cout, Cin, 3, 3) and Cin % G == 0 and G <= 256
+    rt = np.float32 if prec == "f32" else np.float64
+    wq = np.zeros((9, Cout, Cin), np.int8)
+    sw = np.zeros((9, Cout, Cin // G), rt)
+    getattr(lib(), "wq8o_w8a8_quant_w_" + prec)(Cin, Cout, G, _p(w), _p(wq), _p(sw))
+    return wq, sw
+
+
+def direct_w8a8(x, w, pad, G, prec="f32", keep=False):
+    """Group-wise W8A8 direct 3x3 convolution: y [N][Cout][Ho][Wo]."""
+    x = _f32(x)
+    N, Cin, H, W = x.shape
+    Cout = w.shape[0]
+    xq, sx = direct_quant_x(x, G, prec)
+    wq, sw = direct_quant_w(w, G, prec)
+    Ho, Wo = out_size(H, W, pad)
+    rt = np.float32 if prec == "f32" else np.float64
+    y = np.zeros((N, Cout, Ho, Wo), rt)
+    getattr(lib(), "wq8o_w8a8_conv_" + prec)(N, Cin, Cout, H, W, pad, G, _p(xq), _p(sx), _p(wq),
+                                                _p(sw), _p(y))
+    if keep:
+        return dict(xq=xq, sx=sx, wq=wq, sw=sw, y=y)
+    return y

@@ -281,3 +281,83 @@ void SUF(wq8o_sampled)(int m, long T, int Cin, int Cout, int G, const int8_t *Vq
             }
     }
 }
+
+/* ------------------------------------------------------------------------
+ * Group-wise W8A8 direct 3x3 convolution: the non-Winograd baseline the pages
+ * compare against (group-quantized direct kernels, summary page, Fig. 6
+ * caption; "W8A8 without Winograd" in the review page's results). Same
+ * quantizer as above. Readings: activations are quantized per (image, pixel,
+ * group of G consecutive input channels); weights per (kernel tap, output
+ * channel, group of G input channels); the output is one fp32 fma chain per
+ * (image, co, pixel) over taps kh*3+kw ascending, then groups ascending, of
+ * fl(sx * sw) * P with P the exact int32 group dot product; taps that fall
+ * outside the image contribute nothing (zero codes).
+ * Layouts: xq [N][H][W][Cin], sx [N][H][W][Cin/G]; wq [9][Cout][Cin],
+ * sw [9][Cout][Cin/G]; y [N][Cout][Ho][Wo].
+ */
+void SUF(wq8o_w8a8_quant_x)(int N, int Cin, int H, int W, int G, const float *x,
+                              int8_t *xq, REAL *sx)
+{
+    const int ng = Cin / G;
+#pragma omp parallel for schedule(static) collapse(2)
+    for (int img = 0; img < N; ++img)
+        for (int h = 0; h < H; ++h) {
+            REAL buf[256];
+            for (int w = 0; w < W; ++w) {
+                const size_t px = ((size_t)img * H + h) * W + w;
+                for (int gi = 0; gi < ng; ++gi) {
+                    for (int c = 0; c < G; ++c)
+                        buf[c] = (REAL)x[(((size_t)img * Cin + gi * G + c) * H + h) * W + w];
+                    SUF(quantize)(buf, 1, G, xq + px * Cin + (size_t)gi * G, 1, sx + px * ng + gi);
+                }
+            }
+        }
+}
+
+void SUF(wq8o_w8a8_quant_w)(int Cin, int Cout, int G, const float *w, int8_t *wq, REAL *sw)
+{
+    const int ng = Cin / G;
+#pragma omp parallel for schedule(static)
+    for (int co = 0; co < Cout; ++co) {
+        REAL buf[256];
+        for (int tap = 0; tap < 9; ++tap)
+            for (int gi = 0; gi < ng; ++gi) {
+                for (int c = 0; c < G; ++c)
+                    buf[c] = (REAL)w[((size_t)co * Cin + gi * G + c) * 9 + tap];
+                SUF(quantize)(buf, 1, G, wq + ((size_t)tap * Cout + co) * Cin + (size_t)gi * G, 1,
+                              sw + ((size_t)tap * Cout + co) * ng + gi);
+            }
+    }
+}
+
+void SUF(wq8o_w8a8_conv)(int N, int Cin, int Cout, int H, int W, int pad, int G,
+                           const int8_t *xq, const REAL *sx, const int8_t *wq, const REAL *sw,
+                           REAL *y)
+{
+    const int Ho = H + 2 * pad - 2, Wo = W + 2 * pad - 2, ng = Cin / G;
+#pragma omp parallel for schedule(static) collapse(2)
+    for (int img = 0; img < N; ++img)
+        for (int co = 0; co < Cout; ++co)
+            for (int ho = 0; ho < Ho; ++ho)
+                for (int wo = 0; wo < Wo; ++wo) {
+                    REAL acc = 0;
+                    for (int kh = 0; kh < 3; ++kh)
+                        for (int kw = 0; kw < 3; ++kw) {
+                            const int h = ho + kh - pad, w = wo + kw - pad;
+                            if (h < 0 || h >= H || w < 0 || w >= W)
+                                continue;
+                            const int tap = kh * 3 + kw;
+                            const size_t px = ((size_t)img * H + h) * W + w;
+                            const int8_t *a = xq + px * Cin;
+                            const int8_t *b = wq + ((size_t)tap * Cout + co) * Cin;
+                            for (int gi = 0; gi < ng; ++gi) {
+                                int32_t P = 0;
+                                for (int c = gi * G; c < (gi + 1) * G; ++c)
+                                    P += (int32_t)a[c] * (int32_t)b[c];
+                                const REAL s = sx[px * ng + gi] * sw[((size_t)tap * Cout + co) * ng + gi];
+                                acc = FMA(s, (REAL)P, acc);
+                            }
+                        }
+                    y[(((size_t)img * Cout + co) * Ho + ho) * Wo + wo] = acc;
+                }
+}
