@@ -289,9 +289,11 @@ void SUF(wq8o_sampled)(int m, long T, int Cin, int Cout, int G, const int8_t *Vq
  * quantizer as above. Readings: activations are quantized per (image, pixel,
  * group of G consecutive input channels); weights per (kernel tap, output
  * channel, group of G input channels); the output is one fp32 fma chain per
- * (image, co, pixel) over taps kh*3+kw ascending, then groups ascending, of
- * fl(sx * sw) * P with P the exact int32 group dot product; taps that fall
- * outside the image contribute nothing (zero codes).
+ * (image, co, pixel) over groups ascending and, inside each group, taps
+ * kh*3+kw ascending, of fl(sx * sw) * P with P the exact int32 group dot
+ * product (the pages fix no order; group-major lets an implementation hold
+ * one group's scales at a time); taps that fall outside the image contribute
+ * nothing (zero codes).
  * Layouts: xq [N][H][W][Cin], sx [N][H][W][Cin/G]; wq [9][Cout][Cin],
  * sw [9][Cout][Cin/G]; y [N][Cout][Ho][Wo].
  */
@@ -341,23 +343,22 @@ void SUF(wq8o_w8a8_conv)(int N, int Cin, int Cout, int H, int W, int pad, int G,
             for (int ho = 0; ho < Ho; ++ho)
                 for (int wo = 0; wo < Wo; ++wo) {
                     REAL acc = 0;
-                    for (int kh = 0; kh < 3; ++kh)
-                        for (int kw = 0; kw < 3; ++kw) {
-                            const int h = ho + kh - pad, w = wo + kw - pad;
-                            if (h < 0 || h >= H || w < 0 || w >= W)
-                                continue;
-                            const int tap = kh * 3 + kw;
-                            const size_t px = ((size_t)img * H + h) * W + w;
-                            const int8_t *a = xq + px * Cin;
-                            const int8_t *b = wq + ((size_t)tap * Cout + co) * Cin;
-                            for (int gi = 0; gi < ng; ++gi) {
+                    for (int gi = 0; gi < ng; ++gi)
+                        for (int kh = 0; kh < 3; ++kh)
+                            for (int kw = 0; kw < 3; ++kw) {
+                                const int h = ho + kh - pad, w = wo + kw - pad;
+                                if (h < 0 || h >= H || w < 0 || w >= W)
+                                    continue;
+                                const int tap = kh * 3 + kw;
+                                const size_t px = ((size_t)img * H + h) * W + w;
+                                const int8_t *a = xq + px * Cin;
+                                const int8_t *b = wq + ((size_t)tap * Cout + co) * Cin;
                                 int32_t P = 0;
                                 for (int c = gi * G; c < (gi + 1) * G; ++c)
                                     P += (int32_t)a[c] * (int32_t)b[c];
                                 const REAL s = sx[px * ng + gi] * sw[((size_t)tap * Cout + co) * ng + gi];
                                 acc = FMA(s, (REAL)P, acc);
                             }
-                        }
                     y[(((size_t)img * Cout + co) * Ho + ho) * Wo + wo] = acc;
                 }
 }
