@@ -254,10 +254,24 @@ def run_layer(L, algo, steps, warmup, dev):
         if k in ("stage2", "stage23"):
             stages[k]["int8_TOPS"] = round(hop / (v * 1e-3) / 1e12, 2)
             stages[k]["mfma_frac"] = round(hop / (v * 1e-3) / 1e12 / INT8_PEAK_TOPS, 5)
+    # the non-Winograd baseline on the same layer: group-wise W8A8 direct conv
+    Wq, sW = q.wq8_direct_weights_prepare(plan, w)
+    dws = torch.empty(plan.direct_workspace_bytes, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        q.wq8_direct_forward(plan, x, Wq, sW, y=y, workspace=dws)
+    d_ms = time_events(lambda: q.wq8_direct_forward(plan, x, Wq, sW, y=y, workspace=dws), iters, stream)
+    Xq, sX = q.wq8_direct_quantize_x(plan, x)
+    dq_ms = time_events(lambda: q.wq8_direct_quantize_x(plan, x, Xq, sX), iters, stream)
+    dc_ms = time_events(lambda: q.wq8_direct_conv(plan, Xq, sX, Wq, sW, y=y), iters, stream)
+    direct = {"us": round(d_ms * 1e3, 2), "quantize_x_us": round(dq_ms * 1e3, 2),
+              "conv_us": round(dc_ms * 1e3, 2), "TOPS": round(L.direct_ops() / (d_ms * 1e-3) / 1e12, 2),
+              "winograd_speedup": round(d_ms / ms, 3)}
+    del dws, Xq, sX
+
     dom = max(k_ms, key=k_ms.get)
     achieved = nbytes[dom] / (k_ms[dom] * 1e-3) / 1e9
     return dict(plan=plan, d=d, ms=ms, wall=wall, stages=stages, dom=dom, achieved=achieved,
-                nbytes=nbytes, tops=L.direct_ops() / (ms * 1e-3) / 1e12,
+                nbytes=nbytes, tops=L.direct_ops() / (ms * 1e-3) / 1e12, direct=direct,
                 hot=(statistics.median(hot), min(hot)), cold=(statistics.median(cold), min(cold)))
 
 
@@ -296,7 +310,8 @@ def main():
             for algo in ("staged", "fused"):
                 r = run_layer(L, algo, args.steps, args.warmup, dev)
                 print(json.dumps({"layer": name, "algo": algo, "us": round(r["ms"] * 1e3, 2),
-                                  "TOPS": round(r["tops"], 2), "stages": r["stages"]}), flush=True)
+                                  "TOPS": round(r["tops"], 2), "stages": r["stages"],
+                                  "direct_w8a8": r["direct"]}), flush=True)
         return
 
     L = WL.LAYERS[args.layer]
@@ -317,6 +332,7 @@ def main():
                      "traffic": recorded_traffic(L.name, dom),
                      "bytes_per_launch": r["nbytes"][dom]},
         "stages": r["stages"],
+        "baseline_direct_w8a8": r["direct"],
         "per_step_ms": {"median": round(r["hot"][0], 5), "min": round(r["hot"][1], 5),
                         "cold_median": round(r["cold"][0], 5), "cold_min": round(r["cold"][1], 5),
                         "cold_TOPS": round(L.direct_ops() / (r["cold"][0] * 1e-3) / 1e12, 3)},

@@ -154,6 +154,36 @@ wq8_status wq8_stage3(const wq8_plan *plan, const float *M, void *y, int8_t *Yq,
 wq8_status wq8_stage23(const wq8_plan *plan, const int8_t *Vq, const float *sV,
                        const int8_t *Uq, const float *sU, void *y, void *stream);
 
+/* ---- Group-wise W8A8 direct 3x3 convolution: the non-Winograd baseline the
+ * method is compared against (group-quantized direct kernels; summary page,
+ * Fig. 6 caption, and the review page's "W8A8 without Winograd" results).
+ * Uses the plan's N, Cin, Cout, H, W, pad, group and dtypes; the Winograd
+ * fields are not used. Same quantizer as above:
+ *   x codes per (image, pixel, group of G input channels):
+ *     Xq [N][H][W][Cin] int8, sX [N][H][W][Cin/G] f32;
+ *   weights per (kernel tap kh*3+kw, output channel, group):
+ *     Wq [9][Cout][Cin] int8, sW [9][Cout][Cin/G] f32;
+ *   y[img][co][ho][wo] = fp32 fma chain over groups ascending, then taps
+ *     ascending, of fl(sX * sW) * P (P the int32 group dot product of the
+ *     codes; taps outside the image contribute nothing). */
+
+/* Workspace bytes of wq8_direct_forward (Xq | sX) and sizes of Wq and sW. */
+wq8_status wq8_direct_query(const wq8_plan *plan, size_t *workspace_bytes, size_t *w_code_bytes,
+                            size_t *w_scale_bytes);
+/* w [Cout][Cin][3][3] f32 -> Wq, sW (device). */
+wq8_status wq8_direct_weights_prepare(const wq8_plan *plan, const float *w, int8_t *Wq, float *sW,
+                                      void *stream);
+/* x (x_dtype, NCHW) -> Xq, sX. */
+wq8_status wq8_direct_quantize_x(const wq8_plan *plan, const void *x, int8_t *Xq, float *sX,
+                                 void *stream);
+/* Xq, sX, Wq, sW -> y (y_dtype, NCHW). */
+wq8_status wq8_direct_conv(const wq8_plan *plan, const int8_t *Xq, const float *sX,
+                           const int8_t *Wq, const float *sW, void *y, void *stream);
+/* wq8_direct_quantize_x then wq8_direct_conv, with Xq and sX in the workspace. */
+wq8_status wq8_direct_forward(const wq8_plan *plan, const void *x, const int8_t *Wq,
+                              const float *sW, void *y, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
 const char *wq8_status_string(wq8_status status);
 /* Detail of the last error on the calling host thread ("" if none). */
 const char *wq8_last_error(void);

@@ -38,8 +38,9 @@ class wq8_desc(C.Structure):
 
 EXPORTS = ("wq8_plan_create", "wq8_plan_destroy", "wq8_plan_query", "wq8_plan_matrices",
            "wq8_weights_prepare", "wq8_conv_forward", "wq8_stage1", "wq8_stage2",
-           "wq8_stage2_i32", "wq8_stage3", "wq8_stage23", "wq8_status_string",
-           "wq8_last_error")
+           "wq8_stage2_i32", "wq8_stage3", "wq8_stage23", "wq8_direct_query",
+           "wq8_direct_weights_prepare", "wq8_direct_quantize_x", "wq8_direct_conv",
+           "wq8_direct_forward", "wq8_status_string", "wq8_last_error")
 
 _lib = None
 
@@ -67,6 +68,11 @@ def load(path: str = LIB_PATH):
     lib.wq8_stage2_i32.argtypes = [P, P, P, P, P]
     lib.wq8_stage3.argtypes = [P, P, P, P, P, P]
     lib.wq8_stage23.argtypes = [P, P, P, P, P, P, P]
+    lib.wq8_direct_query.argtypes = [P, C.POINTER(S), C.POINTER(S), C.POINTER(S)]
+    lib.wq8_direct_weights_prepare.argtypes = [P, P, P, P, P]
+    lib.wq8_direct_quantize_x.argtypes = [P, P, P, P, P]
+    lib.wq8_direct_conv.argtypes = [P, P, P, P, P, P, P]
+    lib.wq8_direct_forward.argtypes = [P, P, P, P, P, P, S, P]
     lib.wq8_status_string.argtypes = [i]
     lib.wq8_status_string.restype = C.c_char_p
     lib.wq8_last_error.argtypes = []
@@ -137,6 +143,10 @@ class Plan:
         self.T = t.value
         self.ng = Cin // group
         self.fused = al.value == ALGOS["fused"]
+        dws, dwc, dws_ = C.c_size_t(), C.c_size_t(), C.c_size_t()
+        _check(lib.wq8_direct_query(h, C.byref(dws), C.byref(dwc), C.byref(dws_)))
+        self.direct_workspace_bytes, self.direct_w_code_bytes = dws.value, dwc.value
+        self.direct_w_scale_bytes = dws_.value
 
     def __del__(self):
         if getattr(self, "_h", None) is not None and _lib is not None:
@@ -250,3 +260,43 @@ def wq8_stage23(plan: Plan, Vq, sV, Uq, sU, y=None, stream=None):
 def tiles(m, N, H, W, pad):
     Ho, Wo = H + 2 * pad - 2, W + 2 * pad - 2
     return N * math.ceil(Ho / m) * math.ceil(Wo / m)
+
+
+# ---- group-wise W8A8 direct convolution (the non-Winograd baseline)
+def wq8_direct_weights_prepare(plan: Plan, w, Wq=None, sW=None, stream=None):
+    if w.dtype != torch.float32 or tuple(w.shape) != (plan.Cout, plan.Cin, 3, 3):
+        raise ValueError("w must be float32 [Cout][Cin][3][3]")
+    if Wq is None:
+        Wq = torch.empty((9, plan.Cout, plan.Cin), dtype=torch.int8, device=w.device)
+        sW = torch.empty((9, plan.Cout, plan.ng), dtype=torch.float32, device=w.device)
+    _check(load().wq8_direct_weights_prepare(plan.handle, _ptr(w), _ptr(Wq), _ptr(sW), _stream(stream)))
+    return Wq, sW
+
+
+def wq8_direct_quantize_x(plan: Plan, x, Xq=None, sX=None, stream=None):
+    _check_x(plan, x)
+    if Xq is None:
+        Xq = torch.empty((plan.N, plan.H, plan.W, plan.Cin), dtype=torch.int8, device=x.device)
+        sX = torch.empty((plan.N, plan.H, plan.W, plan.ng), dtype=torch.float32, device=x.device)
+    _check(load().wq8_direct_quantize_x(plan.handle, _ptr(x), _ptr(Xq), _ptr(sX), _stream(stream)))
+    return Xq, sX
+
+
+def wq8_direct_conv(plan: Plan, Xq, sX, Wq, sW, y=None, stream=None):
+    if y is None:
+        y = plan.empty_output(Xq.device)
+    _check(load().wq8_direct_conv(plan.handle, _ptr(Xq), _ptr(sX), _ptr(Wq), _ptr(sW), _ptr(y),
+                                  _stream(stream)))
+    return y
+
+
+def wq8_direct_forward(plan: Plan, x, Wq, sW, y=None, workspace=None, stream=None):
+    _check_x(plan, x)
+    if y is None:
+        y = plan.empty_output(x.device)
+    if workspace is None:
+        workspace = torch.empty(plan.direct_workspace_bytes, dtype=torch.uint8, device=x.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load().wq8_direct_forward(plan.handle, _ptr(x), _ptr(Wq), _ptr(sW), _ptr(y),
+                                     _ptr(workspace), nbytes, _stream(stream)))
+    return y

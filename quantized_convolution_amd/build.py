@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libwino_q8_conv.so")
-SOURCES = ["wq8_kernels.hip", "wq8_plan.cpp", "wq8_api.cpp"]
+SOURCES = ["wq8_kernels.hip", "wq8_direct.hip", "wq8_plan.cpp", "wq8_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -119,4 +119,66 @@ wq8_status wq8_stage23(const wq8_plan *p, const int8_t *Vq, const float *sV, con
     return launch_fused23(p->geo, p->mats, p->ydt, Vq, sV, Uq, sU, y, stream);
 }
 
+wq8_status wq8_direct_query(const wq8_plan *p, size_t *workspace_bytes, size_t *w_code_bytes,
+                            size_t *w_scale_bytes) {
+    clear_error();
+    if (!p) return fail(WQ8_ERR_INVALID_ARG, "null plan");
+    if (workspace_bytes) *workspace_bytes = p->d_ws_bytes;
+    if (w_code_bytes) *w_code_bytes = p->d_w_code_bytes;
+    if (w_scale_bytes) *w_scale_bytes = p->d_w_scale_bytes;
+    return WQ8_OK;
+}
+
+wq8_status wq8_direct_weights_prepare(const wq8_plan *p, const float *w, int8_t *Wq, float *sW,
+                                      void *stream) {
+    clear_error();
+    if (!p) return fail(WQ8_ERR_INVALID_ARG, "null plan");
+    WQ8_NEED(w);
+    WQ8_NEED(Wq);
+    WQ8_NEED(sW);
+    return launch_direct_weights(p->geo, w, Wq, sW, stream);
+}
+
+wq8_status wq8_direct_quantize_x(const wq8_plan *p, const void *x, int8_t *Xq, float *sX,
+                                 void *stream) {
+    clear_error();
+    if (!p) return fail(WQ8_ERR_INVALID_ARG, "null plan");
+    WQ8_NEED(x);
+    WQ8_NEED(Xq);
+    WQ8_NEED(sX);
+    return launch_direct_qx(p->geo, p->xdt, x, Xq, sX, stream);
+}
+
+wq8_status wq8_direct_conv(const wq8_plan *p, const int8_t *Xq, const float *sX, const int8_t *Wq,
+                           const float *sW, void *y, void *stream) {
+    clear_error();
+    if (!p) return fail(WQ8_ERR_INVALID_ARG, "null plan");
+    WQ8_NEED(Xq);
+    WQ8_NEED(sX);
+    WQ8_NEED(Wq);
+    WQ8_NEED(sW);
+    WQ8_NEED(y);
+    return launch_direct_conv(p->geo, p->ydt, Xq, sX, Wq, sW, y, stream);
+}
+
+wq8_status wq8_direct_forward(const wq8_plan *p, const void *x, const int8_t *Wq, const float *sW,
+                              void *y, void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    if (!p) return fail(WQ8_ERR_INVALID_ARG, "null plan");
+    WQ8_NEED(x);
+    WQ8_NEED(Wq);
+    WQ8_NEED(sW);
+    WQ8_NEED(y);
+    WQ8_NEED(workspace);
+    if (workspace_bytes < p->d_ws_bytes)
+        return fail(WQ8_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
+                    p->d_ws_bytes);
+    if (x == y) return fail(WQ8_ERR_INVALID_ARG, "x and y must not overlap");
+    char *ws = (char *)workspace;
+    int8_t *Xq = (int8_t *)ws;
+    float *sX = (float *)(ws + p->d_off_sx);
+    WQ8_TRY(launch_direct_qx(p->geo, p->xdt, x, Xq, sX, stream));
+    return launch_direct_conv(p->geo, p->ydt, Xq, sX, Wq, sW, y, stream);
+}
+
 }  // extern "C"

@@ -43,6 +43,9 @@ constexpr uint64_t kAtPattern6 = 0xfe7e7e7e7e7full;
 wq8_status fail(wq8_status st, const char *fmt, ...);
 void clear_error();
 
+// WQ8_OK, or WQ8_ERR_HIP with the pending launch error as detail.
+wq8_status check_launch(const char *what);
+
 // Kernel launchers (wq8_kernels.hip). Each returns WQ8_OK or WQ8_ERR_HIP.
 wq8_status launch_weights(const Geo &g, const Mats &mt, const float *w, int8_t *Uq, float *sU,
                           void *stream);
@@ -56,6 +59,15 @@ wq8_status launch_fused23(const Geo &g, const Mats &mt, wq8_dtype ydt, const int
                           const float *sV, const int8_t *Uq, const float *sU, void *y,
                           void *stream);
 
+// Group-wise W8A8 direct convolution (wq8_direct.hip), the non-Winograd
+// baseline: weights Wq [9][Cout][Cin] / sW [9][Cout][Cin/G], activation codes
+// Xq [N][H][W][Cin] / sX [N][H][W][Cin/G].
+wq8_status launch_direct_weights(const Geo &g, const float *w, int8_t *Wq, float *sW, void *stream);
+wq8_status launch_direct_qx(const Geo &g, wq8_dtype xdt, const void *x, int8_t *Xq, float *sX,
+                            void *stream);
+wq8_status launch_direct_conv(const Geo &g, wq8_dtype ydt, const int8_t *Xq, const float *sX,
+                              const int8_t *Wq, const float *sW, void *y, void *stream);
+
 }  // namespace wq8
 
 struct wq8_plan {
@@ -68,4 +80,6 @@ struct wq8_plan {
     // forward workspace layout (bytes); M is only used by the staged schedule
     size_t off_vq, off_sv, off_m, ws_bytes;
     size_t u_code_bytes, u_scale_bytes;
+    // W8A8 direct convolution: workspace Xq | sX, weight sizes
+    size_t d_off_sx, d_ws_bytes, d_w_code_bytes, d_w_scale_bytes;
 };

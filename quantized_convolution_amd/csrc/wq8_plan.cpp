@@ -435,6 +435,14 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
         p->fused = d->algo == WQ8_ALGO_FUSED;
     }
     p->ws_bytes = p->fused ? p->off_m : p->off_m + (size_t)(n2 * g.T * g.Cout) * 4;
+    // W8A8 direct convolution: workspace Xq | sX, weights Wq / sW
+    {
+        const size_t npx = (size_t)g.N * g.H * g.W;
+        p->d_off_sx = round_up(npx * g.Cin, 256);
+        p->d_ws_bytes = p->d_off_sx + round_up(npx * g.ng * 4, 256);
+        p->d_w_code_bytes = (size_t)9 * g.Cout * g.Cin;
+        p->d_w_scale_bytes = (size_t)9 * g.Cout * g.ng * 4;
+    }
     // every output-channel block reads all activation codes of its tiles and
     // every tile block all weights of its channels: keep the larger operand
     // split across the XCDs' L2s
