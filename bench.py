@@ -202,6 +202,28 @@ def cpu_baseline(L, d, min_seconds=10.0):
             "direct_f64_ms": round(td * 1e3, 1)}
 
 
+def accuracy(L, d, dev, images=4):
+    """Output SQNR (dB) of the GPU forward against a float64 CPU convolution
+    (torch), on the first `images` images, for the timed scales, standard
+    scales (S = I) and equalising scales."""
+    from quantized_convolution_amd import scales as S
+
+    n = L.m + 2
+    x = torch.from_numpy(d["x"][:images]).to(dev)
+    w = torch.from_numpy(d["w"]).to(dev)
+    ref = torch.nn.functional.conv2d(torch.from_numpy(d["x"][:images]).double(),
+                                     torch.from_numpy(d["w"]).double(), padding=L.pad)
+    out = {}
+    for name, (b, g) in {"timed_scales": (d["s_b"], d["s_g"]), "standard_S_I": ([1.0] * n, [1.0] * n),
+                         "equalizing": S.equalizing_scales(L.m, list(d["points"]))}.items():
+        plan = q.Plan(L.m, images, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"], s_B=b, s_G=g)
+        Uq, sU = q.wq8_weights_prepare(plan, w)
+        y = q.wq8_conv_forward(plan, x, Uq, sU).double().cpu()
+        out[name] = round(float(10 * torch.log10(torch.sum(ref ** 2) / torch.sum((y - ref) ** 2))), 2)
+    return {"sqnr_db": out, "reference": "float64 direct convolution (torch, CPU)",
+            "sample": f"images 0..{images - 1} of the timed workload"}
+
+
 def run_layer(L, algo, steps, warmup, dev):
     d = WL.make(L)
     plan = q.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"],
@@ -333,6 +355,7 @@ def main():
                      "bytes_per_launch": r["nbytes"][dom]},
         "stages": r["stages"],
         "baseline_direct_w8a8": r["direct"],
+        "accuracy": accuracy(L, r["d"], dev),
         "per_step_ms": {"median": round(r["hot"][0], 5), "min": round(r["hot"][1], 5),
                         "cold_median": round(r["cold"][0], 5), "cold_min": round(r["cold"][1], 5),
                         "cold_TOPS": round(L.direct_ops() / (r["cold"][0] * 1e-3) / 1e12, 3)},

@@ -1,0 +1,83 @@
+"""Scale generators (quantized_convolution_amd.scales): pinned against the
+test fixture's independent closed form, against the oracle's quantized
+pipeline, and by the effect the pages describe (standard scales collapse an
+F(6,3) layer with one Y scale per tile; equalised or learned scales recover
+it; core claim and Fig. 3 caption of the review page)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from quantized_convolution_amd import scales as S
+from quantized_convolution_amd import workloads as WL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def small_layer(m):
+    return WL.small(WL.LAYERS["c2_f6_n32_c64_56x56_g64"], N=2, H=20, W=20, Cin=64, Cout=32).replace(m=m)
+
+
+def sqnr(L, d, sb, sg):
+    ref = oracle.direct_conv_f64(d["x"], d["w"], L.pad)
+    y = oracle.forward(L.m, d["x"], d["w"], L.pad, L.G, points=S.standard_points(L.m), s_b=sb, s_g=sg)
+    return oracle.sqnr_db(ref, y)
+
+
+@pytest.mark.parametrize("m", [4, 6])
+def test_closed_form_matches_fixture(m):
+    with open(os.path.join(ROOT, "tests", "golden", "equalized_scales.json")) as f:
+        fx = json.load(f)[f"F({m},3)"]
+    sb, sg = S.equalizing_scales(m)
+    np.testing.assert_allclose(sb, fx["s_B"], rtol=2e-7)
+    np.testing.assert_allclose(sg, fx["s_G"], rtol=2e-7)
+
+
+@pytest.mark.parametrize("m", [4, 6])
+def test_empirical_fit_agrees_with_closed_form(m):
+    a = np.array(S.equalizing_scales(m, method="closed")[0]) * np.array(S.equalizing_scales(m)[1])
+    sb, sg = S.equalizing_scales(m, method="empirical", samples=40000)
+    b = np.array(sb) * np.array(sg)
+    # only the product s_B s_G matters for Y; the fit is up to a common factor
+    r = b / a
+    assert np.max(r) / np.min(r) < 1.08
+
+
+@pytest.mark.parametrize("m", [4, 6])
+def test_model_matches_oracle_pipeline(m):
+    """The tools' fake-quantized layer (float64, no straight-through) and the
+    oracle's float64 pipeline quantize at the same points and groups."""
+    import torch
+
+    L = small_layer(m)
+    d = WL.make(L)
+    sb, sg = S.equalizing_scales(m)
+    y_or = oracle.forward(m, d["x"], d["w"], L.pad, L.G, points=S.standard_points(m), s_b=sb, s_g=sg,
+                          prec="f64")
+    y_tool = S._layer_forward(m, S.standard_points(m), torch.log(torch.tensor(sb, dtype=torch.float64)),
+                              torch.log(torch.tensor(sg, dtype=torch.float64)),
+                              torch.from_numpy(d["x"]).double(), torch.from_numpy(d["w"]).double(),
+                              L.G).numpy()
+    # rounding of the transform matrices (exact rationals vs LAPACK) may flip
+    # a code at a tie; outputs otherwise agree to ~1e-12
+    assert oracle.sqnr_db(y_or, y_tool) > 60
+
+
+@pytest.mark.parametrize("m", [4, 6])
+def test_equalizing_scales_recover_collapse(m):
+    L = small_layer(m)
+    d = WL.make(L)
+    n = m + 2
+    s_id = sqnr(L, d, [1.0] * n, [1.0] * n)
+    s_eq = sqnr(L, d, *S.equalizing_scales(m))
+    assert s_eq > s_id + 10.0 and s_eq > 12.0
+
+
+def test_learning_from_identity_recovers_f43():
+    L = small_layer(4)
+    d = WL.make(L)
+    sb, sg, hist = S.learn_scales(4, steps=40, lr=0.1, layers=((1, 64, 16, 16, 16),), init="identity")
+    assert hist[-1] < hist[0] - 10.0
+    assert sqnr(L, d, sb, sg) > sqnr(L, d, [1.0] * 6, [1.0] * 6) + 10.0
