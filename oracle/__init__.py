@@ -54,6 +54,7 @@ def lib():
             getattr(_lib, "wq8o_stage1" + s).argtypes = [i, i, i, i, i, i, i, P, P, P, P]
             getattr(_lib, "wq8o_stage2" + s).argtypes = [i, l, i, i, i, P, P, P, P, P]
             getattr(_lib, "wq8o_stage3" + s).argtypes = [i, i, i, i, i, i, P, P, P, P, P]
+            getattr(_lib, "wq8o_stage3_rows" + s).argtypes = [i, i, i, i, i, i, P, P, P, P, P]
             getattr(_lib, "wq8o_sampled" + s).argtypes = [i, l, i, i, i, P, P, P, P, P, i, P, P, P,
                                                            P, P]
             getattr(_lib, "wq8o_w8a8_quant_x" + s).argtypes = [i, i, i, i, i, P, P, P]
@@ -183,7 +184,10 @@ def stage2_i32(Vq, Uq, G):
     return P
 
 
-def stage3(m, M, N, H, W, pad, At, prec="f32"):
+def stage3(m, M, N, H, W, pad, At, prec="f32", y_group="tile"):
+    """Y requantization + output transform. y_group "tile": one scale per
+    (tile, co) over all taps, sY [T][Cout]; "row": one per row of taps,
+    sY [T][Cout][n]."""
     n2, T, Cout = M.shape
     R = _real(prec)
     M = np.ascontiguousarray(M, R)
@@ -191,9 +195,15 @@ def stage3(m, M, N, H, W, pad, At, prec="f32"):
     Ho, Wo = out_size(H, W, pad)
     y = np.zeros((N, Cout, Ho, Wo), R)
     Yq = np.zeros((T, Cout, n2), np.int8)
-    sY = np.zeros((T, Cout), R)
-    getattr(lib(), "wq8o_stage3_" + prec)(m, N, Cout, H, W, pad, _p(At), _p(M), _p(y),
-                                          _p(Yq), _p(sY))
+    if y_group == "tile":
+        sY = np.zeros((T, Cout), R)
+        fn = "wq8o_stage3_"
+    elif y_group == "row":
+        sY = np.zeros((T, Cout, m + 2), R)
+        fn = "wq8o_stage3_rows_"
+    else:
+        raise ValueError(y_group)
+    getattr(lib(), fn + prec)(m, N, Cout, H, W, pad, _p(At), _p(M), _p(y), _p(Yq), _p(sY))
     return y, Yq, sY
 
 
@@ -217,7 +227,8 @@ def sampled(m, Vq, sV, Uq, sU, At, pairs, prec="f32"):
     return Ms, Yq, sY, ys
 
 
-def forward(m, x, w, pad, G, points=None, s_b=None, s_g=None, prec="f32", keep=False):
+def forward(m, x, w, pad, G, points=None, s_b=None, s_g=None, prec="f32", keep=False,
+            y_group="tile"):
     """Whole quantized pipeline. Returns y, or a dict of every stage if keep."""
     n = m + 2
     points = transforms.standard_points(m) if points is None else points
@@ -229,7 +240,7 @@ def forward(m, x, w, pad, G, points=None, s_b=None, s_g=None, prec="f32", keep=F
     Uq, sU = weights(m, w, G, Gm, prec)
     Vq, sV = stage1(m, x, pad, G, Bt, prec)
     M = stage2(Vq, sV, Uq, sU, G, prec)
-    y, Yq, sY = stage3(m, M, N, H, W, pad, At, prec)
+    y, Yq, sY = stage3(m, M, N, H, W, pad, At, prec, y_group)
     if not keep:
         return y
     return dict(Bt=Bt, G=Gm, At=At, Uq=Uq, sU=sU, Vq=Vq, sV=sV, M=M, Yq=Yq, sY=sY, y=y)

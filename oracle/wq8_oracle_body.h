@@ -362,3 +362,55 @@ void SUF(wq8o_w8a8_conv)(int N, int Cin, int Cout, int H, int W, int pad, int G,
                     y[(((size_t)img * Cout + co) * Ho + ho) * Wo + wo] = acc;
                 }
 }
+
+/* Stage 3 with one Y scale per row of taps: for each (t, co) and row i of
+ * the n x n Winograd-domain tile, quantize M[i*n + j] over j; dequantize
+ * Y^[i][j] = sy_i * Yq[i][j]; then O = A^T Y^ A as fp32 fma chains in index
+ * order (the scales vary by row, so they enter before the transform). The
+ * review page's core claim names "a single or per-row scale" as the two
+ * granularities that cannot hold the cross-shaped range of Y.
+ * sY_out: [T][Cout][n]. */
+void SUF(wq8o_stage3_rows)(int m, int N, int Cout, int H, int W, int pad, const REAL *At,
+                           const REAL *M, REAL *y, int8_t *Yq_out, REAL *sY_out)
+{
+    const int n = m + 2, n2 = n * n;
+    const int Ho = H + 2 * pad - 2, Wo = W + 2 * pad - 2;
+    const int tH = (Ho + m - 1) / m, tW = (Wo + m - 1) / m;
+    const long T = (long)N * tH * tW;
+#pragma omp parallel for schedule(static) collapse(2)
+    for (long t = 0; t < T; ++t)
+        for (int co = 0; co < Cout; ++co) {
+            const int img = (int)(t / ((long)tH * tW));
+            const int ty = (int)(t / tW % tH), tx = (int)(t % tW);
+            int8_t yq[256];
+            REAL sy[16], yd[16][16], z[16][16];
+            for (int i = 0; i < n; ++i) {
+                SUF(quantize)(M + ((size_t)i * n * T + t) * Cout + co, (long)T * Cout, n, yq + i * n, 1,
+                              &sy[i]);
+                for (int j = 0; j < n; ++j)
+                    yd[i][j] = sy[i] * (REAL)yq[i * n + j];
+            }
+            for (int a = 0; a < m; ++a)
+                for (int j = 0; j < n; ++j) {
+                    REAL acc = 0;
+                    for (int i = 0; i < n; ++i)
+                        acc = FMA(At[a * n + i], yd[i][j], acc);
+                    z[a][j] = acc;
+                }
+            for (int a = 0; a < m; ++a)
+                for (int b = 0; b < m; ++b) {
+                    REAL acc = 0;
+                    for (int j = 0; j < n; ++j)
+                        acc = FMA(z[a][j], At[b * n + j], acc);
+                    int h = ty * m + a, ww = tx * m + b;
+                    if (h < Ho && ww < Wo)
+                        y[(((size_t)img * Cout + co) * Ho + h) * Wo + ww] = acc;
+                }
+            if (Yq_out)
+                for (int k = 0; k < n2; ++k)
+                    Yq_out[((size_t)t * Cout + co) * n2 + k] = yq[k];
+            if (sY_out)
+                for (int i = 0; i < n; ++i)
+                    sY_out[((size_t)t * Cout + co) * n + i] = sy[i];
+        }
+}

@@ -177,7 +177,7 @@ def _q(v):
     return np.clip(np.rint(v * inv), -127, 127).astype(np.int8), a / 127.0
 
 
-def kron_pipeline(m, x, w, pad, G, Bt, Gm, At):
+def kron_pipeline(m, x, w, pad, G, Bt, Gm, At, y_group="tile"):
     """Independent formulation on whole tiles: vec(B d B^T) = (B kron B) vec(d)."""
     n = m + 2
     N, Cin, H, W = x.shape
@@ -200,7 +200,7 @@ def kron_pipeline(m, x, w, pad, G, Bt, Gm, At):
     Vq = np.zeros((n * n, T_, Cin), np.int8)
     sV = np.zeros((n * n, T_, ng))
     Yq = np.zeros((T_, Cout, n * n), np.int8)
-    sY = np.zeros((T_, Cout))
+    sY = np.zeros((T_, Cout)) if y_group == "tile" else np.zeros((T_, Cout, n))
     y = np.zeros((N, Cout, tH * m, tW * m))
     t = 0
     for img in range(N):
@@ -218,15 +218,23 @@ def kron_pipeline(m, x, w, pad, G, Bt, Gm, At):
                             sl = slice(g * G, (g + 1) * G)
                             P = int(np.dot(Vq[tap, t, sl].astype(np.int64), Uq[tap, co, sl].astype(np.int64)))
                             Mv[tap] += sV[tap, t, g] * sU[tap, co, g] * P
-                    Yq[t, co], sY[t, co] = _q(Mv)
-                    o = (KA @ Yq[t, co].astype(np.float64)) * sY[t, co]
+                    if y_group == "tile":
+                        Yq[t, co], sY[t, co] = _q(Mv)
+                        o = (KA @ Yq[t, co].astype(np.float64)) * sY[t, co]
+                    else:  # one scale per row of taps, applied before the transform
+                        Yd = np.zeros(n * n)
+                        for i in range(n):
+                            Yq[t, co, i * n:(i + 1) * n], sY[t, co, i] = _q(Mv[i * n:(i + 1) * n])
+                            Yd[i * n:(i + 1) * n] = sY[t, co, i] * Yq[t, co, i * n:(i + 1) * n]
+                        o = KA @ Yd
                     y[img, co, ty * m:(ty + 1) * m, tx * m:(tx + 1) * m] = o.reshape(m, m)
                 t += 1
     return dict(Uq=Uq, sU=sU, Vq=Vq, sV=sV, Yq=Yq, sY=sY, y=y[:, :, :Ho, :Wo])
 
 
+@pytest.mark.parametrize("y_group", ["tile", "row"])
 @pytest.mark.parametrize("m", [4, 6])
-def test_brute_force_kronecker_tiny(m):
+def test_brute_force_kronecker_tiny(m, y_group):
     n = m + 2
     r = np.random.default_rng(40 + m)
     cases = 0
@@ -239,8 +247,9 @@ def test_brute_force_kronecker_tiny(m):
                 x, w = rand_layer(int(r.integers(1 << 30)), 1, C, C, H, W)
                 sb, sg = pert_scales(int(r.integers(1 << 30)), n)
                 Bt, Gm, At = T.transforms_f64(m, T.standard_points(m), sb, sg)
-                ref = kron_pipeline(m, x, w, pad, G, Bt, Gm, At)
-                got = oracle.forward(m, x, w, pad, G, s_b=sb, s_g=sg, prec="f64", keep=True)
+                ref = kron_pipeline(m, x, w, pad, G, Bt, Gm, At, y_group)
+                got = oracle.forward(m, x, w, pad, G, s_b=sb, s_g=sg, prec="f64", keep=True,
+                                     y_group=y_group)
                 for k in ("Uq", "Vq", "Yq"):
                     assert np.array_equal(got[k], ref[k]), (k, C, G, H, W, pad)
                 for k in ("sU", "sV", "sY"):

@@ -81,3 +81,19 @@ def test_learning_from_identity_recovers_f43():
     sb, sg, hist = S.learn_scales(4, steps=40, lr=0.1, layers=((1, 64, 16, 16, 16),), init="identity")
     assert hist[-1] < hist[0] - 10.0
     assert sqnr(L, d, sb, sg) > sqnr(L, d, [1.0] * 6, [1.0] * 6) + 10.0
+
+
+def test_per_row_y_scales_do_not_rescue_standard_f63():
+    """Per-row Y scales with S = I leave F(6,3) collapsed (the review page's
+    core claim names single and per-row scales alike); equalised scales
+    recover it under either granularity. Absolute values are unpinned."""
+    L = small_layer(6)
+    d = WL.make(L)
+    ref = oracle.direct_conv_f64(d["x"], d["w"], L.pad)
+    out = {}
+    for yg in ("tile", "row"):
+        for nm, (b, g) in {"I": ([1.0] * 8, [1.0] * 8), "eq": S.equalizing_scales(6)}.items():
+            y = oracle.forward(6, d["x"], d["w"], L.pad, L.G, s_b=b, s_g=g, y_group=yg)
+            out[yg, nm] = oracle.sqnr_db(ref, y)
+    assert out["row", "I"] < 5.0 and out["tile", "I"] < 0.0
+    assert out["row", "eq"] > out["row", "I"] + 10 and out["tile", "eq"] > out["tile", "I"] + 10
