@@ -86,6 +86,15 @@ typedef enum { WQ8_F32 = 0, WQ8_BF16 = 1 } wq8_dtype;
  *           costs less than writing and reading M, else STAGED. */
 typedef enum { WQ8_ALGO_AUTO = 0, WQ8_ALGO_STAGED = 1, WQ8_ALGO_FUSED = 2 } wq8_algo;
 
+/* Granularity of the Y (Winograd-domain output) scales. TILE: one scale per
+ * (tile, output channel) spanning all n*n taps (the default; the
+ * tap-spanning scale whose cross-shaped range the learned S_B, S_G even out;
+ * core claim and Fig. 3 caption of the review page). ROW: one scale per row
+ * of taps (the other granularity the core claim names); the dequantized
+ * Y^[i][j] = sy_i Yq[i][j] then enters A^T Y^ A. ROW runs the staged
+ * schedule only. */
+typedef enum { WQ8_YGROUP_TILE = 0, WQ8_YGROUP_ROW = 1 } wq8_ygroup;
+
 typedef struct wq8_plan wq8_plan; /* opaque */
 
 typedef struct {
@@ -101,6 +110,7 @@ typedef struct {
     wq8_dtype x_dtype;     /* activations in */
     wq8_dtype y_dtype;     /* activations out */
     wq8_algo algo;         /* stage 2 + 3 schedule for wq8_conv_forward */
+    wq8_ygroup y_group;    /* Y scale granularity (TILE unless stated) */
 } wq8_desc;
 
 /* Validates the descriptor and builds the scaled transforms on the host (exact
@@ -144,13 +154,14 @@ wq8_status wq8_stage2(const wq8_plan *plan, const int8_t *Vq, const float *sV,
 /* int32 partial sums P [n*n][Cin/G][T][Cout], one per quantization group. */
 wq8_status wq8_stage2_i32(const wq8_plan *plan, const int8_t *Vq, const int8_t *Uq,
                           int32_t *P, void *stream);
-/* Y requantization + output transform. Yq [T][Cout][n*n] and sY [T][Cout] are
- * optional outputs (NULL to skip). */
+/* Y requantization + output transform. Yq [T][Cout][n*n] and sY ([T][Cout],
+ * or [T][Cout][n] for WQ8_YGROUP_ROW) are optional outputs (NULL to skip). */
 wq8_status wq8_stage3(const wq8_plan *plan, const float *M, void *y, int8_t *Yq,
                       float *sY, void *stream);
 
 /* Stages 2 and 3 as the single fused kernel (M stays on chip): the same Y
- * codes as wq8_stage2 followed by wq8_stage3; y as described for FUSED. */
+ * codes as wq8_stage2 followed by wq8_stage3; y as described for FUSED.
+ * WQ8_ERR_UNSUPPORTED for a WQ8_YGROUP_ROW plan. */
 wq8_status wq8_stage23(const wq8_plan *plan, const int8_t *Vq, const float *sV,
                        const int8_t *Uq, const float *sU, void *y, void *stream);
 

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libwino_q8_conv.so")
 
 WQ8_F32, WQ8_BF16 = 0, 1
 ALGOS = {"auto": 0, "staged": 1, "fused": 2}
+YGROUPS = {"tile": 0, "row": 1}
 _DT = {torch.float32: WQ8_F32, torch.bfloat16: WQ8_BF16}
 
 
@@ -33,7 +34,7 @@ class wq8_desc(C.Structure):
                 ("s_B", C.POINTER(C.c_float)), ("s_G", C.POINTER(C.c_float)),
                 ("group", C.c_int), ("N", C.c_int), ("Cin", C.c_int), ("Cout", C.c_int),
                 ("H", C.c_int), ("W", C.c_int), ("pad", C.c_int),
-                ("x_dtype", C.c_int), ("y_dtype", C.c_int), ("algo", C.c_int)]
+                ("x_dtype", C.c_int), ("y_dtype", C.c_int), ("algo", C.c_int), ("y_group", C.c_int)]
 
 
 EXPORTS = ("wq8_plan_create", "wq8_plan_destroy", "wq8_plan_query", "wq8_plan_matrices",
@@ -110,11 +111,11 @@ class Plan:
     """Owns a wq8_plan handle and the geometry needed to size buffers."""
 
     def __init__(self, m, N, Cin, Cout, H, W, pad=1, group=64, points=None, s_B=None, s_G=None,
-                 x_dtype=torch.float32, y_dtype=None, algo="auto"):
+                 x_dtype=torch.float32, y_dtype=None, algo="auto", y_group="tile"):
         lib = load()
         n = m + 2
         self.m, self.n, self.N, self.Cin, self.Cout, self.H, self.W = m, n, N, Cin, Cout, H, W
-        self.pad, self.group, self.algo = pad, group, algo
+        self.pad, self.group, self.algo, self.y_group = pad, group, algo, y_group
         self.x_dtype = x_dtype
         self.y_dtype = x_dtype if y_dtype is None else y_dtype
         self.Ho, self.Wo = H + 2 * pad - 2, W + 2 * pad - 2
@@ -131,7 +132,7 @@ class Plan:
 
         d = wq8_desc(m, arr(points, C.c_double, np.float64), arr(s_B, C.c_float, np.float32),
                      arr(s_G, C.c_float, np.float32), group, N, Cin, Cout, H, W, pad,
-                     _DT[self.x_dtype], _DT[self.y_dtype], ALGOS[algo])
+                     _DT[self.x_dtype], _DT[self.y_dtype], ALGOS[algo], YGROUPS[y_group])
         h = C.c_void_p()
         self._h = None
         _check(wq8_plan_create(d, h))
@@ -244,7 +245,8 @@ def wq8_stage3(plan: Plan, M, y=None, Yq=None, sY=None, want_codes=False, stream
         y = plan.empty_output(M.device)
     if want_codes and Yq is None:
         Yq = torch.empty((plan.T, plan.Cout, plan.n * plan.n), dtype=torch.int8, device=M.device)
-        sY = torch.empty((plan.T, plan.Cout), dtype=torch.float32, device=M.device)
+        sshape = (plan.T, plan.Cout, plan.n) if plan.y_group == "row" else (plan.T, plan.Cout)
+        sY = torch.empty(sshape, dtype=torch.float32, device=M.device)
     _check(load().wq8_stage3(plan.handle, _ptr(M), _ptr(y), _ptr(Yq), _ptr(sY), _stream(stream)))
     return (y, Yq, sY) if want_codes else y
 

@@ -116,6 +116,7 @@ wq8_status wq8_stage23(const wq8_plan *p, const int8_t *Vq, const float *sV, con
     WQ8_NEED(Uq);
     WQ8_NEED(sU);
     WQ8_NEED(y);
+    if (p->geo.y_rows) return fail(WQ8_ERR_UNSUPPORTED, "per-row Y scales run the staged schedule only");
     return launch_fused23(p->geo, p->mats, p->ydt, Vq, sV, Uq, sU, y, stream);
 }
 

@@ -29,6 +29,7 @@ struct Geo {
     int co_major;             // fused kernel: 1 = output-channel blocks outermost
                               // (weights larger than the activation codes)
     int fused_waves;          // fused kernel: waves per block (4 or 16)
+    int y_rows;               // 1: one Y scale per row of taps (staged only)
 };
 
 // Nonzero patterns of B^T [n][n] and A^T [m][n] for the standard points

@@ -593,8 +593,10 @@ __global__ __launch_bounds__(256) void k_stage2(const int8_t *__restrict__ Vq,
 }
 
 // ------------------------------------------ Y requant + output transform
-// One thread per (tile, co); consecutive threads take consecutive co.
-template <int M, typename YT>
+// One thread per (tile, co); consecutive threads take consecutive co. ROWS:
+// one Y scale per row of taps, applied to the codes before the transform;
+// otherwise one scale over all taps, applied to the result.
+template <int M, bool ROWS, typename YT>
 __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT *__restrict__ y,
                                                 int8_t *__restrict__ Yq, float *__restrict__ sY,
                                                 Mats mt, Geo g) {
@@ -604,27 +606,43 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
     const int co = (int)(idx % g.Cout), t = (int)(idx / g.Cout);
     const size_t plane = (size_t)g.T * g.Cout;
     float mv[NT];
-    float a = 0.0f;
 #pragma unroll
-    for (int tap = 0; tap < NT; ++tap) {
-        mv[tap] = Mi[tap * plane + idx];
-        a = fmaxf(a, fabsf(mv[tap]));
-    }
+    for (int tap = 0; tap < NT; ++tap) mv[tap] = Mi[tap * plane + idx];
+    // quantize taps [k0, k0 + len) with one scale
     int q[NT];
+    float yd[NT];  // ROWS: dequantized codes
+    auto quant = [&](int k0, int len) {
+        float a = 0.0f;
+        for (int k = k0; k < k0 + len; ++k) a = fmaxf(a, fabsf(mv[k]));
+        float s = 0.0f;
+        if (a != 0.0f) {
+            const float inv = 127.0f / a;
+            for (int k = k0; k < k0 + len; ++k) q[k] = quant_code(mv[k], inv);
+            s = a / 127.0f;
+        } else {
+            for (int k = k0; k < k0 + len; ++k) q[k] = 0;
+        }
+        return s;
+    };
     float s = 0.0f;
-    if (a != 0.0f) {
-        const float inv = 127.0f / a;
+    if constexpr (ROWS) {
 #pragma unroll
-        for (int tap = 0; tap < NT; ++tap) q[tap] = quant_code(mv[tap], inv);
-        s = a / 127.0f;
+        for (int i = 0; i < N; ++i) {
+            const float si = quant(i * N, N);
+#pragma unroll
+            for (int j = 0; j < N; ++j) yd[i * N + j] = si * (float)q[i * N + j];
+            if (sY) sY[idx * N + i] = si;
+        }
+        s = 1.0f;
     } else {
+        s = quant(0, NT);
 #pragma unroll
-        for (int tap = 0; tap < NT; ++tap) q[tap] = 0;
+        for (int k = 0; k < NT; ++k) yd[k] = (float)q[k];
+        if (sY) sY[idx] = s;
     }
     if (Yq)
 #pragma unroll
         for (int tap = 0; tap < NT; ++tap) Yq[idx * NT + tap] = (int8_t)q[tap];
-    if (sY) sY[idx] = s;
 
     float z[M][N];
 #pragma unroll
@@ -633,7 +651,7 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
         for (int j = 0; j < N; ++j) {
             float acc = 0.0f;
 #pragma unroll
-            for (int i = 0; i < N; ++i) acc = __builtin_fmaf(mt.At[aa * N + i], (float)q[i * N + j], acc);
+            for (int i = 0; i < N; ++i) acc = __builtin_fmaf(mt.At[aa * N + i], yd[i * N + j], acc);
             z[aa][j] = acc;
         }
     const int tx = t % g.tW, rr = t / g.tW, ty = rr % g.tH, img = rr / g.tH;
@@ -646,7 +664,7 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
 #pragma unroll
             for (int j = 0; j < N; ++j) acc = __builtin_fmaf(z[aa][j], mt.At[b * N + j], acc);
             const int h = ty * M + aa, w = tx * M + b;
-            if (h < g.Ho && w < g.Wo) store_act(yp + (size_t)h * g.Wo + w, acc * s);
+            if (h < g.Ho && w < g.Wo) store_act(yp + (size_t)h * g.Wo + w, ROWS ? acc : acc * s);
         }
 }
 
@@ -1161,7 +1179,8 @@ static void stage3_m(const Geo &g, const Mats &mt, const float *Mi, YT *y, int8_
                      hipStream_t s) {
     const int64_t work = (int64_t)g.T * g.Cout;
     dim3 grid((unsigned)((work + 255) / 256));
-    hipLaunchKernelGGL((k_stage3<M, YT>), grid, dim3(256), 0, s, Mi, y, Yq, sY, mt, g);
+    if (g.y_rows) hipLaunchKernelGGL((k_stage3<M, true, YT>), grid, dim3(256), 0, s, Mi, y, Yq, sY, mt, g);
+    else hipLaunchKernelGGL((k_stage3<M, false, YT>), grid, dim3(256), 0, s, Mi, y, Yq, sY, mt, g);
 }
 
 template <int M, int G, typename YT>

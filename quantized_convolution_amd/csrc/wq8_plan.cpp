@@ -425,7 +425,14 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
     p->u_scale_bytes = (size_t)(n2 * g.Cout * g.ng) * 4;
     if (d->algo != WQ8_ALGO_AUTO && d->algo != WQ8_ALGO_STAGED && d->algo != WQ8_ALGO_FUSED)
         return fail(WQ8_ERR_INVALID_ARG, "unknown algo %d", (int)d->algo);
-    if (d->algo == WQ8_ALGO_AUTO) {
+    if (d->y_group != WQ8_YGROUP_TILE && d->y_group != WQ8_YGROUP_ROW)
+        return fail(WQ8_ERR_INVALID_ARG, "unknown y_group %d", (int)d->y_group);
+    g.y_rows = d->y_group == WQ8_YGROUP_ROW;
+    if (g.y_rows && d->algo == WQ8_ALGO_FUSED)
+        return fail(WQ8_ERR_UNSUPPORTED, "per-row Y scales run the staged schedule only");
+    if (g.y_rows) {
+        p->fused = 0;
+    } else if (d->algo == WQ8_ALGO_AUTO) {
         // the fused kernel re-reads the weights once per 16-tile block (from
         // L2 / Infinity Cache when they fit); the staged one writes and reads M
         const double reread = (double)p->u_code_bytes * (double)((g.T + 15) / 16);

@@ -45,3 +45,22 @@ def test_gpu_sqnr_collapse_and_recovery(dev, m):
         assert abs(s_gpu - s_or) < 0.05
         got[name] = s_gpu
     assert got["equalizing"] > got["standard"] + 10 and got["learned"] > got["standard"] + 10
+
+
+def test_gpu_per_row_scales_stay_collapsed_f63(dev):
+    """Per-row Y scales with S = I: F(6,3) stays collapsed on the GPU path
+    as in the oracle; equalised scales recover it."""
+    L = WL.small(WL.LAYERS["c2_f6_n32_c64_56x56_g64"], N=2, H=26, W=26, Cin=64, Cout=32)
+    d = WL.make(L)
+    ref = oracle.direct_conv_f64(d["x"], d["w"], L.pad)
+    got = {}
+    for name, (b, g) in {"standard": ([1.0] * 8, [1.0] * 8), "equalizing": S.equalizing_scales(6)}.items():
+        plan = q.Plan(6, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, s_B=b, s_G=g, y_group="row")
+        Uq, sU = q.wq8_weights_prepare(plan, torch.from_numpy(d["w"]).to(dev))
+        y = q.wq8_conv_forward(plan, torch.from_numpy(d["x"]).to(dev), Uq, sU)
+        torch.cuda.synchronize()
+        got[name] = oracle.sqnr_db(ref, y.cpu().numpy())
+        s_or = oracle.sqnr_db(ref, oracle.forward(6, d["x"], d["w"], L.pad, L.G, s_b=b, s_g=g, y_group="row"))
+        print(f"\n[case] F(6,3) per-row {name}: SQNR gpu {got[name]:.2f} dB, oracle {s_or:.2f} dB", flush=True)
+        assert abs(got[name] - s_or) < 0.05
+    assert got["standard"] < 5.0 and got["equalizing"] > got["standard"] + 10

@@ -294,3 +294,31 @@ def test_fused_block_shapes(dev, monkeypatch, waves, name, kw):
     y = q.wq8_conv_forward(plan, to_dev(d["x"], dev), Uq, sU)
     torch.cuda.synchronize()
     assert_out(y.cpu().numpy(), ref, f"fused forward, {waves} waves")
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("c2_f6_n32_c64_56x56_g64", dict(N=2, H=17, W=23, Cin=64, Cout=24)),
+    ("c4_f4_n2_c320_64x64_g64_pert", dict(N=1, H=13, W=9, Cin=128, Cout=20)),
+])
+def test_per_row_y_scales(dev, name, kw):
+    """One Y scale per row of taps (staged schedule): Y codes and scales
+    bit-exact from the oracle's M; forward output within tolerance; the
+    fused entry point refuses the plan."""
+    L = WL.small(WL.LAYERS[name], **kw)
+    print(f"\n[case] per-row Y {L.name}", flush=True)
+    d = WL.make(L)
+    ref = oracle.forward(L.m, d["x"], d["w"], L.pad, L.G, points=list(d["points"]), s_b=d["s_b"],
+                         s_g=d["s_g"], keep=True, y_group="row")
+    plan = q.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"], s_B=d["s_b"],
+                  s_G=d["s_g"], y_group="row")
+    assert not plan.fused
+    y3, Yq, sY = q.wq8_stage3(plan, to_dev(ref["M"], dev), want_codes=True)
+    Uq, sU = q.wq8_weights_prepare(plan, to_dev(d["w"], dev))
+    y = q.wq8_conv_forward(plan, to_dev(d["x"], dev), Uq, sU)
+    torch.cuda.synchronize()
+    assert np.array_equal(Yq.cpu().numpy(), ref["Yq"]) and np.array_equal(sY.cpu().numpy(), ref["sY"])
+    assert_out(y3.cpu().numpy(), ref["y"], "per-row stage 3")
+    assert_out(y.cpu().numpy(), ref["y"], "per-row forward")
+    with pytest.raises(q.Wq8Error) as e:
+        q.wq8_stage23(plan, *q.wq8_stage1(plan, to_dev(d["x"], dev)), Uq, sU)
+    assert e.value.status == -2

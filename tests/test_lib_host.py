@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def _create(**kw):
     base = dict(m=6, points=None, s_B=None, s_G=None, group=64, N=1, Cin=64, Cout=64, H=16, W=16,
-                pad=1, x_dtype=0, y_dtype=0, algo=0)
+                pad=1, x_dtype=0, y_dtype=0, algo=0, y_group=0)
     base.update(kw)
     keep = []
 
@@ -53,7 +53,7 @@ def _create(**kw):
     d = B.wq8_desc(base["m"], arr(base["points"], C.c_double, np.float64),
                    arr(base["s_B"], C.c_float, np.float32), arr(base["s_G"], C.c_float, np.float32),
                    base["group"], base["N"], base["Cin"], base["Cout"], base["H"], base["W"],
-                   base["pad"], base["x_dtype"], base["y_dtype"], base["algo"])
+                   base["pad"], base["x_dtype"], base["y_dtype"], base["algo"], base["y_group"])
     h = C.c_void_p()
     st = B.wq8_plan_create(d, h)
     if st == 0:
@@ -71,6 +71,8 @@ def _create(**kw):
     (dict(H=1, W=1, pad=0), -1), (dict(H=1, W=1, pad=1), 0),
     (dict(N=0), -1), (dict(Cout=0), -1),
     (dict(x_dtype=7), -1), (dict(algo=3), -1), (dict(algo=1), 0), (dict(algo=2), 0),
+    (dict(y_group=1), 0), (dict(y_group=2), -1), (dict(y_group=1, algo=2), -2),
+    (dict(y_group=1, algo=1), 0),
     (dict(points=[0, 1, -1, 2, 2, .5, -.5, math.inf]), -3),
     (dict(points=[0, 1, -1, 2, -2, .5, math.inf, math.inf]), -3),
     (dict(points=[0, 1, -1, 2, -2, .5, -.5, math.nan]), -1),
