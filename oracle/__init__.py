@@ -52,6 +52,9 @@ def lib():
         for s in ("_f32", "_f64"):
             getattr(_lib, "wq8o_weights" + s).argtypes = [i, i, i, i, P, P, P, P]
             getattr(_lib, "wq8o_stage1" + s).argtypes = [i, i, i, i, i, i, i, P, P, P, P]
+            getattr(_lib, "wq8o_quant_bt" + s).argtypes = [i, i, P, P, P]
+            getattr(_lib, "wq8o_stage1_int" + s).argtypes = [i, i, i, i, i, i, i, P, P, P, P, P,
+                                                             P, P]
             getattr(_lib, "wq8o_stage2" + s).argtypes = [i, l, i, i, i, P, P, P, P, P]
             getattr(_lib, "wq8o_stage3" + s).argtypes = [i, i, i, i, i, i, P, P, P, P, P]
             getattr(_lib, "wq8o_stage3_rows" + s).argtypes = [i, i, i, i, i, i, P, P, P, P, P]
@@ -164,6 +167,43 @@ def stage1(m, x, pad, G, Bt, prec="f32"):
     return Vq, sV
 
 
+IN_QUANT = ("fp32", "int_tensor", "int_row")
+
+
+def quant_bt(Bt, rows, prec="f32"):
+    """B^T quantized for the literal input stage: Bq [n][n] int8 and sB [n]
+    (one scale per row when rows, else one for the matrix, repeated)."""
+    R = _real(prec)
+    Bt = np.ascontiguousarray(Bt, R)
+    n = Bt.shape[0]
+    Bq = np.zeros((n, n), np.int8)
+    sB = np.zeros(n, R)
+    getattr(lib(), "wq8o_quant_bt_" + prec)(n, int(bool(rows)), _p(Bt), _p(Bq), _p(sB))
+    return Bq, sB
+
+
+def stage1_int(m, x, pad, G, Bq, sB, prec="f32", keep=False):
+    """Literal input stage: patch codes per (tile, group) and an integer
+    transform with Bq; returns Vq, sV (and xq [T][Cin][n][n], sx [T][Cin/G]
+    when keep)."""
+    x = _f32(x)
+    N, Cin, H, W = x.shape
+    _, _, T = tiles(m, N, H, W, pad)
+    n = m + 2
+    R = _real(prec)
+    Bq = np.ascontiguousarray(Bq, np.int8)
+    sB = np.ascontiguousarray(sB, R)
+    Vq = np.zeros((n * n, T, Cin), np.int8)
+    sV = np.zeros((n * n, T, Cin // G), R)
+    xq = np.zeros((T, Cin, n, n), np.int8)
+    sx = np.zeros((T, Cin // G), R)
+    getattr(lib(), "wq8o_stage1_int_" + prec)(m, N, Cin, H, W, pad, G, _p(Bq), _p(sB), _p(x),
+                                               _p(Vq), _p(sV), _p(xq), _p(sx))
+    if keep:
+        return Vq, sV, xq, sx
+    return Vq, sV
+
+
 def stage2(Vq, sV, Uq, sU, G, prec="f32"):
     n2, T, Cin = Vq.shape
     Cout = Uq.shape[1]
@@ -228,8 +268,10 @@ def sampled(m, Vq, sV, Uq, sU, At, pairs, prec="f32"):
 
 
 def forward(m, x, w, pad, G, points=None, s_b=None, s_g=None, prec="f32", keep=False,
-            y_group="tile"):
-    """Whole quantized pipeline. Returns y, or a dict of every stage if keep."""
+            y_group="tile", in_quant="fp32"):
+    """Whole quantized pipeline. Returns y, or a dict of every stage if keep.
+    in_quant "fp32": fp32 input transform; "int_tensor" / "int_row": the
+    literal input stage with B^T quantized per matrix / per row."""
     n = m + 2
     points = transforms.standard_points(m) if points is None else points
     s_b = np.ones(n, np.float32) if s_b is None else s_b
@@ -238,7 +280,13 @@ def forward(m, x, w, pad, G, points=None, s_b=None, s_g=None, prec="f32", keep=F
     Bt, Gm, At = mk(m, points, s_b, s_g)
     N, _, H, W = x.shape
     Uq, sU = weights(m, w, G, Gm, prec)
-    Vq, sV = stage1(m, x, pad, G, Bt, prec)
+    if in_quant == "fp32":
+        Vq, sV = stage1(m, x, pad, G, Bt, prec)
+    elif in_quant in IN_QUANT:
+        Bq, sB = quant_bt(Bt, in_quant == "int_row", prec)
+        Vq, sV = stage1_int(m, x, pad, G, Bq, sB, prec)
+    else:
+        raise ValueError(in_quant)
     M = stage2(Vq, sV, Uq, sU, G, prec)
     y, Yq, sY = stage3(m, M, N, H, W, pad, At, prec, y_group)
     if not keep:

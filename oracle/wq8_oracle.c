@@ -14,6 +14,9 @@
  *   wq8o_stage2_i32        per-group int32 Hadamard partial sums
  *   wq8o_{weights,stage1,stage2,stage3}_{f32,f64}
  *                          the fixed-order quantized pipeline
+ *   wq8o_{quant_bt,stage1_int}_{f32,f64}
+ *                          the literal input stage (quantized B^T and input,
+ *                          integer transform)
  *
  * Transform matrices (Bt, G, At) are inputs: they are built in exact rational
  * arithmetic by oracle/transforms.py and rounded once to fp32/fp64.

@@ -154,6 +154,106 @@ void SUF(wq8o_stage1)(int m, int N, int Cin, int H, int W, int pad, int G,
 }
 
 /*
+ * Literal reading of the input stage. The review page's Eqs. 14-16 survive
+ * only as the combined factor "sqB sqB sqx": a scale of the transform matrix
+ * on the left, the same on the right, and a scale of the input. Read plainly,
+ * B^T and the input patch are both quantized, the input transform runs on
+ * their integer codes, and the three scales bring the result back to real
+ * values; V is then quantized per group as in wq8o_stage1.
+ *
+ * B^T quantization (same absmax quantizer): rows == 0 gives one scale for the
+ * whole n x n matrix, rows == 1 one scale per row. sB[i] is the scale of row
+ * i (all equal for rows == 0).
+ *   Bt : [n][n]  ->  Bq [n][n] int8,  sB [n]
+ */
+void SUF(wq8o_quant_bt)(int n, int rows, const REAL *Bt, int8_t *Bq, REAL *sB)
+{
+    if (rows) {
+        for (int i = 0; i < n; ++i)
+            SUF(quantize)(Bt + (size_t)i * n, 1, n, Bq + (size_t)i * n, 1, &sB[i]);
+    } else {
+        REAL s;
+        SUF(quantize)(Bt, 1, n * n, Bq, 1, &s);
+        for (int i = 0; i < n; ++i)
+            sB[i] = s;
+    }
+}
+
+/*
+ * Stage 1, literal reading. For every tile t and group of G input channels,
+ * the n x n patches of the group's channels (zero outside the image) share
+ * one scale sx[t][g] (absmax over all n*n*G values) and codes dq. Then per
+ * channel
+ *   W[i][j] = sum_k sum_l Bq[i][k] dq[k][l] Bq[j][l]      (exact integers)
+ *   V[i][j] = float(W[i][j]) * ((sB[i] * sB[j]) * sx)     (REAL, in that order)
+ * and V is quantized per (tap, t, group) as in wq8o_stage1.
+ *   xq : [T][Cin][n][n] int8 patch codes and sx : [T][Cin/G], optional (NULL).
+ */
+void SUF(wq8o_stage1_int)(int m, int N, int Cin, int H, int W, int pad, int G,
+                          const int8_t *Bq, const REAL *sB, const float *x,
+                          int8_t *Vq, REAL *sV, int8_t *xq, REAL *sx)
+{
+    const int n = m + 2, n2 = n * n, ng = Cin / G;
+    const int Ho = H + 2 * pad - 2, Wo = W + 2 * pad - 2;
+    const int tH = (Ho + m - 1) / m, tW = (Wo + m - 1) / m;
+    const long T = (long)N * tH * tW;
+#pragma omp parallel for schedule(static)
+    for (long t = 0; t < T; ++t) {
+        const int img = (int)(t / ((long)tH * tW));
+        const int ty = (int)(t / tW % tH), tx = (int)(t % tW);
+        REAL *V = (REAL *)malloc(sizeof(REAL) * (size_t)n2 * Cin);     /* [tap][ci] */
+        REAL *d = (REAL *)malloc(sizeof(REAL) * (size_t)G * n2);       /* [c][k][l] */
+        int8_t *dq = (int8_t *)malloc((size_t)G * n2);
+        for (int gi = 0; gi < ng; ++gi) {
+            for (int c = 0; c < G; ++c) {
+                const int ci = gi * G + c;
+                for (int k = 0; k < n; ++k)
+                    for (int l = 0; l < n; ++l) {
+                        int h = ty * m - pad + k, ww = tx * m - pad + l;
+                        d[(size_t)c * n2 + k * n + l] =
+                            (h >= 0 && h < H && ww >= 0 && ww < W)
+                                ? (REAL)x[(((size_t)img * Cin + ci) * H + h) * W + ww]
+                                : 0;
+                    }
+            }
+            REAL s;
+            SUF(quantize)(d, 1, G * n2, dq, 1, &s);
+            if (sx)
+                sx[t * ng + gi] = s;
+            if (xq)
+                memcpy(xq + ((size_t)t * Cin + (size_t)gi * G) * n2, dq, (size_t)G * n2);
+            for (int c = 0; c < G; ++c) {
+                const int8_t *p = dq + (size_t)c * n2;
+                long t1[16][16];
+                for (int i = 0; i < n; ++i)
+                    for (int l = 0; l < n; ++l) {
+                        long acc = 0;
+                        for (int k = 0; k < n; ++k)
+                            acc += (long)Bq[i * n + k] * p[k * n + l];
+                        t1[i][l] = acc;
+                    }
+                for (int i = 0; i < n; ++i)
+                    for (int j = 0; j < n; ++j) {
+                        long acc = 0;
+                        for (int l = 0; l < n; ++l)
+                            acc += t1[i][l] * Bq[j * n + l];
+                        const REAL cij = (sB[i] * sB[j]) * s;
+                        V[(size_t)(i * n + j) * Cin + gi * G + c] = (REAL)acc * cij;
+                    }
+            }
+        }
+        for (int tap = 0; tap < n2; ++tap)
+            for (int gi = 0; gi < ng; ++gi)
+                SUF(quantize)(V + (size_t)tap * Cin + (size_t)gi * G, 1, G,
+                              Vq + ((size_t)tap * T + t) * Cin + (size_t)gi * G, 1,
+                              sV + ((size_t)tap * T + t) * ng + gi);
+        free(dq);
+        free(d);
+        free(V);
+    }
+}
+
+/*
  * Stage 2: Hadamard product summed over input channels (Eq. 5), per tap:
  *   P_g = sum_{ci in group g} Vq * Uq            (exact int32)
  *   M   = fma(sV_g * sU_g, P_g, M) for g = 0, 1, ...  starting from +0
