@@ -214,14 +214,20 @@ def accuracy(L, d, dev, images=4):
     ref = torch.nn.functional.conv2d(torch.from_numpy(d["x"][:images]).double(),
                                      torch.from_numpy(d["w"]).double(), padding=L.pad)
     out = {}
-    for name, (b, g) in {"timed_scales": (d["s_b"], d["s_g"]), "standard_S_I": ([1.0] * n, [1.0] * n),
-                         "equalizing": S.equalizing_scales(L.m, list(d["points"]))}.items():
-        plan = q.Plan(L.m, images, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"], s_B=b, s_G=g)
-        Uq, sU = q.wq8_weights_prepare(plan, w)
-        y = q.wq8_conv_forward(plan, x, Uq, sU).double().cpu()
-        out[name] = round(float(10 * torch.log10(torch.sum(ref ** 2) / torch.sum((y - ref) ** 2))), 2)
+    for iq in ("fp32", "int_tensor", "int_row"):
+        row = {}
+        for name, (b, g) in {"timed_scales": (d["s_b"], d["s_g"]), "standard_S_I": ([1.0] * n, [1.0] * n),
+                             "equalizing": S.equalizing_scales(L.m, list(d["points"]))}.items():
+            plan = q.Plan(L.m, images, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"], s_B=b,
+                          s_G=g, in_quant=iq)
+            Uq, sU = q.wq8_weights_prepare(plan, w)
+            y = q.wq8_conv_forward(plan, x, Uq, sU).double().cpu()
+            row[name] = round(float(10 * torch.log10(torch.sum(ref ** 2) / torch.sum((y - ref) ** 2))), 2)
+        out[iq + "_input"] = row
     return {"sqnr_db": out, "reference": "float64 direct convolution (torch, CPU)",
-            "sample": f"images 0..{images - 1} of the timed workload"}
+            "sample": f"images 0..{images - 1} of the timed workload",
+            "input_stage": "fp32: fp32 input transform; int_tensor / int_row: B^T (one scale / one per "
+                           "row) and input patches quantized, integer transform"}
 
 
 def run_layer(L, algo, steps, warmup, dev):
@@ -276,6 +282,18 @@ def run_layer(L, algo, steps, warmup, dev):
         if k in ("stage2", "stage23"):
             stages[k]["int8_TOPS"] = round(hop / (v * 1e-3) / 1e12, 2)
             stages[k]["mfma_frac"] = round(hop / (v * 1e-3) / 1e12 / INT8_PEAK_TOPS, 5)
+    # the literal input stage (quantized B^T and input patch, integer
+    # transform): its stage-1 kernel and whole forward on the same workload
+    lit = {}
+    for iq in ("int_tensor", "int_row"):
+        pl = q.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"], s_B=d["s_b"],
+                    s_G=d["s_g"], algo=algo, in_quant=iq)
+        s1 = time_events(lambda: q.wq8_stage1(pl, x, Vq, sV), iters, stream)
+        fw = time_events(lambda: q.wq8_conv_forward(pl, x, Uq, sU, y=y, workspace=ws), iters, stream)
+        lit[iq] = {"stage1_us": round(s1 * 1e3, 2),
+                   "stage1_hbm_frac": round(nbytes["stage1"] / (s1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "forward_us": round(fw * 1e3, 2),
+                   "TOPS": round(L.direct_ops() / (fw * 1e-3) / 1e12, 2)}
     # the non-Winograd baseline on the same layer: group-wise W8A8 direct conv
     Wq, sW = q.wq8_direct_weights_prepare(plan, w)
     dws = torch.empty(plan.direct_workspace_bytes, dtype=torch.uint8, device=dev)
@@ -293,7 +311,7 @@ def run_layer(L, algo, steps, warmup, dev):
     dom = max(k_ms, key=k_ms.get)
     achieved = nbytes[dom] / (k_ms[dom] * 1e-3) / 1e9
     return dict(plan=plan, d=d, ms=ms, wall=wall, stages=stages, dom=dom, achieved=achieved,
-                nbytes=nbytes, tops=L.direct_ops() / (ms * 1e-3) / 1e12, direct=direct,
+                nbytes=nbytes, tops=L.direct_ops() / (ms * 1e-3) / 1e12, direct=direct, literal=lit,
                 hot=(statistics.median(hot), min(hot)), cold=(statistics.median(cold), min(cold)))
 
 
@@ -333,7 +351,8 @@ def main():
                 r = run_layer(L, algo, args.steps, args.warmup, dev)
                 print(json.dumps({"layer": name, "algo": algo, "us": round(r["ms"] * 1e3, 2),
                                   "TOPS": round(r["tops"], 2), "stages": r["stages"],
-                                  "direct_w8a8": r["direct"]}), flush=True)
+                                  "direct_w8a8": r["direct"], "literal_input_stage": r["literal"]}),
+                      flush=True)
         return
 
     L = WL.LAYERS[args.layer]
@@ -355,6 +374,7 @@ def main():
                      "bytes_per_launch": r["nbytes"][dom]},
         "stages": r["stages"],
         "baseline_direct_w8a8": r["direct"],
+        "literal_input_stage": r["literal"],
         "accuracy": accuracy(L, r["d"], dev),
         "per_step_ms": {"median": round(r["hot"][0], 5), "min": round(r["hot"][1], 5),
                         "cold_median": round(r["cold"][0], 5), "cold_min": round(r["cold"][1], 5),

@@ -95,6 +95,23 @@ typedef enum { WQ8_ALGO_AUTO = 0, WQ8_ALGO_STAGED = 1, WQ8_ALGO_FUSED = 2 } wq8_
  * schedule only. */
 typedef enum { WQ8_YGROUP_TILE = 0, WQ8_YGROUP_ROW = 1 } wq8_ygroup;
 
+/* What the input transform quantizes. The review page's Eqs. 14-16 survive
+ * only as the combined factor "sqB sqB sqx" (a B^T scale on each side and an
+ * input scale; minor comments), so two readings are offered:
+ *   FP32:       V = B^T d B in fp32 fma chains (the default; no quantizer
+ *               before the transform);
+ *   INT_TENSOR: B^T quantized with one scale for the matrix (codes Bq, row
+ *               scale sq_i all equal), the n x n input patches of a (tile,
+ *               group of G input channels) with one scale sx over all n*n*G
+ *               values (zero padding included; codes dq). The transform then
+ *               runs exactly on integers and is scaled back:
+ *                 Wi[i][j] = sum_k sum_l Bq[i][k] dq[k][l] Bq[j][l]  (int32)
+ *                 V[i][j]  = float(Wi[i][j]) * ((sq_i * sq_j) * sx)  (fp32, RNE)
+ *               after which V is quantized per group exactly as for FP32;
+ *   INT_ROW:    as INT_TENSOR with one scale per row of B^T.
+ * Only stage 1 changes; stages 2 and 3 and every layout stay as they are. */
+typedef enum { WQ8_INQ_FP32 = 0, WQ8_INQ_INT_TENSOR = 1, WQ8_INQ_INT_ROW = 2 } wq8_inq;
+
 typedef struct wq8_plan wq8_plan; /* opaque */
 
 typedef struct {
@@ -111,6 +128,7 @@ typedef struct {
     wq8_dtype y_dtype;     /* activations out */
     wq8_algo algo;         /* stage 2 + 3 schedule for wq8_conv_forward */
     wq8_ygroup y_group;    /* Y scale granularity (TILE unless stated) */
+    wq8_inq in_quant;      /* input-stage reading (FP32 unless stated) */
 } wq8_desc;
 
 /* Validates the descriptor and builds the scaled transforms on the host (exact
@@ -130,6 +148,12 @@ wq8_status wq8_plan_query(const wq8_plan *plan, size_t *workspace_bytes,
 /* Host copies of the fp32 matrices the kernels use: Bt [n][n] (carries S_B),
  * G [n][3] (carries S_G), At [m][n] (carries S_A). Any pointer may be NULL. */
 wq8_status wq8_plan_matrices(const wq8_plan *plan, float *Bt, float *G, float *At);
+
+/* Host copies of the quantized B^T used by the INT_TENSOR / INT_ROW input
+ * stage: Bq [n][n] int8 and its row scales sq [n] (fp32 absmax quantizer as
+ * above, over the whole matrix or per row). WQ8_ERR_INVALID_ARG for an FP32
+ * plan. Either pointer may be NULL. */
+wq8_status wq8_plan_bt_codes(const wq8_plan *plan, int8_t *Bq, float *sq);
 
 /* Offline weight transform and quantization (U = G g G^T; per-group int8).
  *   w  [Cout][Cin][3][3] f32 (device), Uq [n*n][Cout][Cin] int8 (device),

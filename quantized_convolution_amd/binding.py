@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libwino_q8_conv.so")
 WQ8_F32, WQ8_BF16 = 0, 1
 ALGOS = {"auto": 0, "staged": 1, "fused": 2}
 YGROUPS = {"tile": 0, "row": 1}
+IN_QUANTS = {"fp32": 0, "int_tensor": 1, "int_row": 2}
 _DT = {torch.float32: WQ8_F32, torch.bfloat16: WQ8_BF16}
 
 
@@ -34,10 +35,12 @@ class wq8_desc(C.Structure):
                 ("s_B", C.POINTER(C.c_float)), ("s_G", C.POINTER(C.c_float)),
                 ("group", C.c_int), ("N", C.c_int), ("Cin", C.c_int), ("Cout", C.c_int),
                 ("H", C.c_int), ("W", C.c_int), ("pad", C.c_int),
-                ("x_dtype", C.c_int), ("y_dtype", C.c_int), ("algo", C.c_int), ("y_group", C.c_int)]
+                ("x_dtype", C.c_int), ("y_dtype", C.c_int), ("algo", C.c_int), ("y_group", C.c_int),
+                ("in_quant", C.c_int)]
 
 
 EXPORTS = ("wq8_plan_create", "wq8_plan_destroy", "wq8_plan_query", "wq8_plan_matrices",
+           "wq8_plan_bt_codes",
            "wq8_weights_prepare", "wq8_conv_forward", "wq8_stage1", "wq8_stage2",
            "wq8_stage2_i32", "wq8_stage3", "wq8_stage23", "wq8_direct_query",
            "wq8_direct_weights_prepare", "wq8_direct_quantize_x", "wq8_direct_conv",
@@ -62,6 +65,7 @@ def load(path: str = LIB_PATH):
     lib.wq8_plan_query.argtypes = [P, C.POINTER(S), C.POINTER(S), C.POINTER(S), C.POINTER(C.c_int64),
                                    C.POINTER(C.c_int)]
     lib.wq8_plan_matrices.argtypes = [P, P, P, P]
+    lib.wq8_plan_bt_codes.argtypes = [P, P, P]
     lib.wq8_weights_prepare.argtypes = [P, P, P, P, P]
     lib.wq8_conv_forward.argtypes = [P, P, P, P, P, P, S, P]
     lib.wq8_stage1.argtypes = [P, P, P, P, P]
@@ -111,11 +115,13 @@ class Plan:
     """Owns a wq8_plan handle and the geometry needed to size buffers."""
 
     def __init__(self, m, N, Cin, Cout, H, W, pad=1, group=64, points=None, s_B=None, s_G=None,
-                 x_dtype=torch.float32, y_dtype=None, algo="auto", y_group="tile"):
+                 x_dtype=torch.float32, y_dtype=None, algo="auto", y_group="tile",
+                 in_quant="fp32"):
         lib = load()
         n = m + 2
         self.m, self.n, self.N, self.Cin, self.Cout, self.H, self.W = m, n, N, Cin, Cout, H, W
         self.pad, self.group, self.algo, self.y_group = pad, group, algo, y_group
+        self.in_quant = in_quant
         self.x_dtype = x_dtype
         self.y_dtype = x_dtype if y_dtype is None else y_dtype
         self.Ho, self.Wo = H + 2 * pad - 2, W + 2 * pad - 2
@@ -132,7 +138,8 @@ class Plan:
 
         d = wq8_desc(m, arr(points, C.c_double, np.float64), arr(s_B, C.c_float, np.float32),
                      arr(s_G, C.c_float, np.float32), group, N, Cin, Cout, H, W, pad,
-                     _DT[self.x_dtype], _DT[self.y_dtype], ALGOS[algo], YGROUPS[y_group])
+                     _DT[self.x_dtype], _DT[self.y_dtype], ALGOS[algo], YGROUPS[y_group],
+                     IN_QUANTS[in_quant])
         h = C.c_void_p()
         self._h = None
         _check(wq8_plan_create(d, h))
@@ -186,6 +193,16 @@ def wq8_plan_matrices(plan: Plan):
     _check(load().wq8_plan_matrices(plan.handle, Bt.ctypes.data_as(C.c_void_p),
                                     Gm.ctypes.data_as(C.c_void_p), At.ctypes.data_as(C.c_void_p)))
     return Bt, Gm, At
+
+
+def wq8_plan_bt_codes(plan: Plan):
+    """Bq [n][n] int8 and row scales sq [n] of an integer-input-stage plan."""
+    n = plan.n
+    Bq = np.zeros((n, n), np.int8)
+    sq = np.zeros(n, np.float32)
+    _check(load().wq8_plan_bt_codes(plan.handle, Bq.ctypes.data_as(C.c_void_p),
+                                    sq.ctypes.data_as(C.c_void_p)))
+    return Bq, sq
 
 
 def wq8_weights_prepare(plan: Plan, w, Uq=None, sU=None, stream=None):

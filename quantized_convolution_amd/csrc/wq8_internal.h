@@ -16,6 +16,8 @@ struct Mats {
     float G[kMaxN * 3];       // [n][3]  carries S_G
     float At[6 * kMaxN];      // [m][n]  carries S_A
     float kscale, oscale;     // 2^-s and 2^s with max |A^T (x) A^T| * 2^-s <= 2^14
+    int Bq[kMaxN * kMaxN];    // [n][n] int8 codes of B^T (integer input stage only)
+    float sqb[kMaxN];         // their row scales
 };
 
 // Problem geometry shared by every kernel.
@@ -30,6 +32,7 @@ struct Geo {
                               // (weights larger than the activation codes)
     int fused_waves;          // fused kernel: waves per block (4 or 16)
     int y_rows;               // 1: one Y scale per row of taps (staged only)
+    int in_quant;             // wq8_inq: 0 fp32 input transform, 1/2 integer
 };
 
 // Nonzero patterns of B^T [n][n] and A^T [m][n] for the standard points

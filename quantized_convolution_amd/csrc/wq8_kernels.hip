@@ -312,7 +312,12 @@ __device__ __forceinline__ void s1_commit(float *win, const S1Loads<M, G, TPB> &
     }
 }
 
-template <int M, int G, int TPB, uint64_t BMASK, bool VEC, typename XT>
+// IQ selects the integer input stage: the patches of a (tile, group) share one
+// absmax scale sx, the transform runs on their codes and the codes of B^T
+// (mt.Bq) in exact int32 arithmetic (24-bit multiplies: |codes| <= 127 and
+// the first pass stays below n * 127^2 < 2^23), and
+// V = float(Wi) * ((sq_i * sq_j) * sx) goes on to the same V quantization.
+template <int M, int G, int TPB, uint64_t BMASK, bool VEC, typename XT, bool IQ>
 __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW)) void k_stage1(
     const XT *__restrict__ x, int8_t *__restrict__ Vq, float *__restrict__ sV, Mats mt, Geo g) {
     constexpr int N = M + 2, NT = N * N;
@@ -322,6 +327,7 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW)) void k_stage1(
     __shared__ float win[SS::CPB * SS::CS];
     __shared__ float red[S::GW > 1 ? SS::NW : 1][64];
     __shared__ __attribute__((aligned(16))) float inv_lds[SS::NW][64 / S::SEG][64];
+    __shared__ float redx[IQ && S::GW > 1 ? SS::NW : 1];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int tl = wave / S::GW;                // this wave's tile in the strip
@@ -354,7 +360,53 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW)) void k_stage1(
         }
 
         float v[NT];
-        {
+        if constexpr (IQ) {
+            float ax = 0.0f;
+#pragma unroll
+            for (int k = 0; k < N; ++k)
+#pragma unroll
+                for (int l = 0; l < N; ++l) ax = fmaxf(ax, fabsf(d[k][l]));
+            ax = seg_max<S::SEG>(ax);
+            if constexpr (S::GW > 1) {
+                if (lane == 0) redx[wave] = ax;
+                __syncthreads();
+                const int w0 = (wave / S::GW) * S::GW;
+                ax = redx[w0];
+#pragma unroll
+                for (int k = 1; k < S::GW; ++k) ax = fmaxf(ax, redx[w0 + k]);
+            }
+            float invx = 0.0f, sx = 0.0f;
+            if (ax != 0.0f) {
+                invx = 127.0f / ax;
+                sx = ax / 127.0f;
+            }
+            int dq[N][N];
+#pragma unroll
+            for (int k = 0; k < N; ++k)
+#pragma unroll
+                for (int l = 0; l < N; ++l) dq[k][l] = (int)__builtin_rintf(d[k][l] * invx);
+            int t1[N][N];
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+#pragma unroll
+                for (int l = 0; l < N; ++l) {
+                    int acc = 0;
+#pragma unroll
+                    for (int k = 0; k < N; ++k)
+                        if ((BMASK >> (i * N + k)) & 1) acc += __mul24(mt.Bq[i * N + k], dq[k][l]);
+                    t1[i][l] = acc;
+                }
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+#pragma unroll
+                for (int j = 0; j < N; ++j) {
+                    int acc = 0;
+#pragma unroll
+                    for (int l = 0; l < N; ++l)
+                        if ((BMASK >> (j * N + l)) & 1) acc += __mul24(t1[i][l], mt.Bq[j * N + l]);
+                    v[i * N + j] = (float)acc * ((mt.sqb[i] * mt.sqb[j]) * sx);
+                }
+        } else {
             float t1[N][N];
 #pragma unroll
             for (int i = 0; i < N; ++i)
@@ -1108,19 +1160,26 @@ wq8_status launch_weights(const Geo &g, const Mats &mt, const float *w, int8_t *
     return check_launch("weight transform");
 }
 
-template <int M, int G, int TPB, uint64_t BMASK, typename XT>
-static void stage1_launch(const Geo &g, const Mats &mt, const XT *x, int8_t *Vq, float *sV,
-                          hipStream_t s) {
+template <int M, int G, int TPB, uint64_t BMASK, typename XT, bool IQ>
+static void stage1_launch_q(const Geo &g, const Mats &mt, const XT *x, int8_t *Vq, float *sV,
+                            hipStream_t s) {
     using SS = S1Shape<M, G, TPB>;
     const int nstrip = (g.tW + TPB - 1) / TPB;
     const int chunks = (g.Cin + SS::CPB - 1) / SS::CPB;
     const unsigned blocks = (unsigned)(nstrip * g.N * g.tH * chunks);
     if (g.W % 4 == 0)
-        hipLaunchKernelGGL((k_stage1<M, G, TPB, BMASK, true, XT>), dim3(blocks), dim3(64 * SS::NW), 0, s,
-                           x, Vq, sV, mt, g);
-    else
-        hipLaunchKernelGGL((k_stage1<M, G, TPB, BMASK, false, XT>), dim3(blocks), dim3(64 * SS::NW), 0,
+        hipLaunchKernelGGL((k_stage1<M, G, TPB, BMASK, true, XT, IQ>), dim3(blocks), dim3(64 * SS::NW), 0,
                            s, x, Vq, sV, mt, g);
+    else
+        hipLaunchKernelGGL((k_stage1<M, G, TPB, BMASK, false, XT, IQ>), dim3(blocks), dim3(64 * SS::NW),
+                           0, s, x, Vq, sV, mt, g);
+}
+
+template <int M, int G, int TPB, uint64_t BMASK, typename XT>
+static void stage1_launch(const Geo &g, const Mats &mt, const XT *x, int8_t *Vq, float *sV,
+                          hipStream_t s) {
+    if (g.in_quant) stage1_launch_q<M, G, TPB, BMASK, XT, true>(g, mt, x, Vq, sV, s);
+    else stage1_launch_q<M, G, TPB, BMASK, XT, false>(g, mt, x, Vq, sV, s);
 }
 
 template <int M, int G, typename XT>

@@ -417,6 +417,30 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
         g.at_std = (at_nz & ~at_pat) == 0;
     }
 
+    // integer input stage: B^T codes and row scales (fp32 absmax quantizer)
+    if (d->in_quant != WQ8_INQ_FP32 && d->in_quant != WQ8_INQ_INT_TENSOR &&
+        d->in_quant != WQ8_INQ_INT_ROW)
+        return fail(WQ8_ERR_INVALID_ARG, "unknown in_quant %d", (int)d->in_quant);
+    g.in_quant = (int)d->in_quant;
+    if (g.in_quant != WQ8_INQ_FP32) {
+        const bool rows = g.in_quant == WQ8_INQ_INT_ROW;
+        for (int r0 = 0; r0 < n; r0 += rows ? 1 : n) {
+            const int len = rows ? n : n * n;
+            float a = 0.0f;
+            for (int i = 0; i < len; ++i) a = fmaxf(a, fabsf(mt.Bt[r0 * n + i]));
+            float sc = 0.0f, inv = 0.0f;
+            if (a != 0.0f) {
+                inv = 127.0f / a;
+                sc = a / 127.0f;
+            }
+            for (int i = 0; i < len; ++i) {
+                const float r = rintf(mt.Bt[r0 * n + i] * inv);
+                mt.Bq[r0 * n + i] = (int)fminf(fmaxf(r, -127.0f), 127.0f);
+            }
+            for (int i = 0; i < (rows ? 1 : n); ++i) mt.sqb[r0 + i] = sc;
+        }
+    }
+
     // workspace: Vq | sV | M, each 256-byte aligned
     p->off_vq = 0;
     p->off_sv = round_up((size_t)(n2 * g.T * g.Cin), 256);
@@ -507,6 +531,18 @@ wq8_status wq8_plan_matrices(const wq8_plan *p, float *Bt, float *G, float *At) 
     if (Bt) memcpy(Bt, p->mats.Bt, sizeof(float) * n * n);
     if (G) memcpy(G, p->mats.G, sizeof(float) * n * 3);
     if (At) memcpy(At, p->mats.At, sizeof(float) * m * n);
+    return WQ8_OK;
+}
+
+wq8_status wq8_plan_bt_codes(const wq8_plan *p, int8_t *Bq, float *sq) {
+    wq8::clear_error();
+    if (!p) return wq8::fail(WQ8_ERR_INVALID_ARG, "null plan");
+    if (p->geo.in_quant == WQ8_INQ_FP32)
+        return wq8::fail(WQ8_ERR_INVALID_ARG, "the plan's input stage does not quantize B^T");
+    const int n = p->geo.n;
+    if (Bq)
+        for (int i = 0; i < n * n; ++i) Bq[i] = (int8_t)p->mats.Bq[i];
+    if (sq) memcpy(sq, p->mats.sqb, sizeof(float) * n);
     return WQ8_OK;
 }
 

@@ -64,3 +64,32 @@ def test_gpu_per_row_scales_stay_collapsed_f63(dev):
         print(f"\n[case] F(6,3) per-row {name}: SQNR gpu {got[name]:.2f} dB, oracle {s_or:.2f} dB", flush=True)
         assert abs(got[name] - s_or) < 0.05
     assert got["standard"] < 5.0 and got["equalizing"] > got["standard"] + 10
+
+
+@pytest.mark.parametrize("m", [4, 6])
+@pytest.mark.parametrize("iq", ["int_tensor", "int_row"])
+def test_gpu_literal_input_stage_accuracy(dev, m, iq):
+    """The literal input stage (B^T and input patch quantized, integer
+    transform) on the GPU path: SQNR equal to the oracle's for standard and
+    equalising scales; equalising scales still recover the layer, and the
+    extra input quantization costs at most 1 dB against the fp32 input
+    transform (the error sits in Y, not in the input stage: core claim)."""
+    L = WL.small(WL.LAYERS["c2_f6_n32_c64_56x56_g64"], N=2, H=26, W=26, Cin=64, Cout=32).replace(m=m)
+    d = WL.make(L)
+    n = m + 2
+    ref = oracle.direct_conv_f64(d["x"], d["w"], L.pad)
+    got = {}
+    for name, (b, g) in {"standard": ([1.0] * n, [1.0] * n), "equalizing": S.equalizing_scales(m)}.items():
+        for mode in ("fp32", iq):
+            plan = q.Plan(m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, s_B=b, s_G=g, in_quant=mode)
+            Uq, sU = q.wq8_weights_prepare(plan, torch.from_numpy(d["w"]).to(dev))
+            y = q.wq8_conv_forward(plan, torch.from_numpy(d["x"]).to(dev), Uq, sU)
+            torch.cuda.synchronize()
+            got[name, mode] = oracle.sqnr_db(ref, y.cpu().numpy())
+            s_or = oracle.sqnr_db(ref, oracle.forward(m, d["x"], d["w"], L.pad, L.G, s_b=b, s_g=g,
+                                                       in_quant=mode))
+            print(f"\n[case] F({m},3) {name} input {mode}: SQNR gpu {got[name, mode]:.2f} dB, "
+                  f"oracle {s_or:.2f} dB", flush=True)
+            assert abs(got[name, mode] - s_or) < 0.05
+    assert got["equalizing", iq] > got["standard", iq] + 10
+    assert got["equalizing", iq] > got["equalizing", "fp32"] - 1.0

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def _create(**kw):
     base = dict(m=6, points=None, s_B=None, s_G=None, group=64, N=1, Cin=64, Cout=64, H=16, W=16,
-                pad=1, x_dtype=0, y_dtype=0, algo=0, y_group=0)
+                pad=1, x_dtype=0, y_dtype=0, algo=0, y_group=0, in_quant=0)
     base.update(kw)
     keep = []
 
@@ -53,7 +53,8 @@ def _create(**kw):
     d = B.wq8_desc(base["m"], arr(base["points"], C.c_double, np.float64),
                    arr(base["s_B"], C.c_float, np.float32), arr(base["s_G"], C.c_float, np.float32),
                    base["group"], base["N"], base["Cin"], base["Cout"], base["H"], base["W"],
-                   base["pad"], base["x_dtype"], base["y_dtype"], base["algo"], base["y_group"])
+                   base["pad"], base["x_dtype"], base["y_dtype"], base["algo"], base["y_group"],
+                   base["in_quant"])
     h = C.c_void_p()
     st = B.wq8_plan_create(d, h)
     if st == 0:
@@ -73,6 +74,8 @@ def _create(**kw):
     (dict(x_dtype=7), -1), (dict(algo=3), -1), (dict(algo=1), 0), (dict(algo=2), 0),
     (dict(y_group=1), 0), (dict(y_group=2), -1), (dict(y_group=1, algo=2), -2),
     (dict(y_group=1, algo=1), 0),
+    (dict(in_quant=1), 0), (dict(in_quant=2, algo=2), 0), (dict(in_quant=3), -1),
+    (dict(in_quant=-1), -1),
     (dict(points=[0, 1, -1, 2, 2, .5, -.5, math.inf]), -3),
     (dict(points=[0, 1, -1, 2, -2, .5, math.inf, math.inf]), -3),
     (dict(points=[0, 1, -1, 2, -2, .5, -.5, math.nan]), -1),
@@ -115,6 +118,30 @@ def test_plan_matrices_equal_exactly_rounded(m):
         assert np.array_equal(Bt, rb), name
         assert np.array_equal(Gm, rg), name
         assert np.array_equal(At, ra), name
+
+
+@pytest.mark.parametrize("m", [4, 6])
+@pytest.mark.parametrize("iq", ["int_tensor", "int_row"])
+def test_plan_bt_codes_match_oracle(m, iq):
+    """The host's B^T quantization for the integer input stage equals the
+    oracle's (same fp32 absmax quantizer, per matrix or per row)."""
+    import oracle
+    n = m + 2
+    for name, sb, sg in _scale_sets():
+        sb, sg = sb[:n], sg[:n]
+        plan = B.Plan(m, 1, 16, 16, 9, 9, 1, 16, s_B=sb, s_G=sg, in_quant=iq)
+        Bq, sq = B.wq8_plan_bt_codes(plan)
+        Bt, _, _ = B.wq8_plan_matrices(plan)
+        rq, rs = oracle.quant_bt(Bt, iq == "int_row")
+        assert np.array_equal(Bq, rq), name
+        assert np.array_equal(sq, rs), name
+
+
+def test_plan_bt_codes_rejects_fp32_plan():
+    plan = B.Plan(6, 1, 16, 16, 9, 9, 1, 16)
+    with pytest.raises(B.Wq8Error) as e:
+        B.wq8_plan_bt_codes(plan)
+    assert e.value.status == -1
 
 
 def test_plan_query_sizes():
