@@ -60,6 +60,19 @@ def recorded_traffic(layer, kernel):
     return None if k is None else k["bytes_per_launch"]
 
 
+def stage_of(kernel_name):
+    """Stage key of a kernel in a rocprofv3 trace, or None. The stage-1
+    kernel with the integer input stage (last template argument true) is
+    "stage1_int"."""
+    for stage, prefix in KERNEL_NAMES.items():
+        i = kernel_name.find(prefix)
+        if i >= 0:
+            if stage == "stage1" and kernel_name[i + len(prefix):].split(">")[0].rstrip().endswith("true"):
+                return "stage1_int"
+            return stage
+    return None
+
+
 def _pmc_rows(d, counter):
     """(kernel name, value) of every dispatch in a rocprofv3 --pmc CSV run."""
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -91,9 +104,9 @@ def traffic_summary(layer, fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mi
     fetch, write = _pmc_rows(fetch_dir, "FETCH_SIZE"), _pmc_rows(write_dir, "WRITE_SIZE")
     lines = ["| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (scaled) |",
              "|---|---|---|---|---|"]
-    for stage, prefix in KERNEL_NAMES.items():
-        f = [v for k, v in fetch if prefix in k]
-        w = [v for k, v in write if prefix in k]
+    for stage in list(KERNEL_NAMES) + ["stage1_int"]:
+        f = [v for k, v in fetch if stage_of(k) == stage]
+        w = [v for k, v in write if stage_of(k) == stage]
         if not f or not w:
             continue
         fk, wk = statistics.median(f), statistics.median(w)
