@@ -478,13 +478,11 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
     // every tile block all weights of its channels: keep the larger operand
     // split across the XCDs' L2s
     p->geo.co_major = p->u_code_bytes > (size_t)(n2 * g.T * g.Cin);
-    // fused kernel: 4-wave blocks (taps split 4 ways) fill the GPU's wave slots
-    // when there are many 16 x 16 blocks; with few, 16-wave blocks keep four
-    // times as many loads in flight
+    // fused kernel: 4-wave blocks (taps split 4 ways). WQ8_FUSED_WAVES=16
+    // selects 16-wave blocks (4 taps per wave), kept for comparison: they were
+    // slower on every benchmark layer.
     {
-        const int64_t nblk = ((g.T + 15) / 16) * (int64_t)((g.Cout + 15) / 16);
         const char *ov = getenv("WQ8_FUSED_WAVES");
-        (void)nblk;
         p->geo.fused_waves = ov && atoi(ov) == 16 ? 16 : 4;
     }
     return WQ8_OK;
