@@ -30,7 +30,7 @@ struct Geo {
                               // points' matrices do (zero terms may be skipped)
     int co_major;             // fused kernel: 1 = output-channel blocks outermost
                               // (weights larger than the activation codes)
-    int fused_waves;          // fused kernel: waves per block (4 or 16)
+    int fused_waves;          // fused kernel: waves per block (4, 8 or 16)
     int y_rows;               // 1: one Y scale per row of taps (staged only)
     int in_quant;             // wq8_inq: 0 fp32 input transform, 1/2 integer
 };

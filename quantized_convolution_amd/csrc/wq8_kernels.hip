@@ -939,8 +939,10 @@ __global__ __launch_bounds__(64 * WPB, WPB == 4 && MULTI ? 3 : 4) void k_fused23
     };
     // Two batches of taps in flight: the next batch's loads (of this group or,
     // when a group has an even number of batches, of the next group) are
-    // issued before the current batch's MFMAs and dequantization.
+    // issued before the current batch's MFMAs and dequantization. With 8
+    // waves per block a wave's 8 taps of a group are loaded at once.
     constexpr int BATCH = KSTEPS >= 2 ? 1
+                          : WPB == 8 ? TPW
                           : TPW % 4 == 0 && TPW / 4 % 2 == 0 && !K64 ? 4
                           : TPW % 2 == 0 ? 2 : TPW % 3 == 0 ? 3 : 1;
     constexpr int NB = TPW / BATCH;
@@ -1246,9 +1248,16 @@ template <int M, int G, typename YT>
 static void fused_m_g(const Geo &g, const Mats &mt, const int8_t *Vq, const float *sV,
                       const int8_t *Uq, const float *sU, YT *y, hipStream_t s) {
     const unsigned blocks = (unsigned)(((g.T + 15) / 16) * ((g.Cout + 15) / 16));
-    // 16 waves per block when 4-wave blocks would leave most wave slots idle
-    // (few tiles, many channels): more loads in flight per CU
+    // waves per block as the plan chose (8 or 16 split the taps further; F(4,3)
+    // has 36 taps and always uses 4)
     if constexpr (M == 6) {
+        if (g.fused_waves == 8) {
+            if (g.ng == 1)
+                hipLaunchKernelGGL((k_fused23<M, G, 8, false, YT>), dim3(blocks), dim3(512), 0, s, Vq, sV, Uq, sU, y, mt, g);
+            else
+                hipLaunchKernelGGL((k_fused23<M, G, 8, true, YT>), dim3(blocks), dim3(512), 0, s, Vq, sV, Uq, sU, y, mt, g);
+            return;
+        }
         if (g.fused_waves == 16) {
             if (g.ng == 1)
                 hipLaunchKernelGGL((k_fused23<M, G, 16, false, YT>), dim3(blocks), dim3(1024), 0, s, Vq, sV, Uq, sU, y, mt, g);

@@ -478,12 +478,19 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
     // every tile block all weights of its channels: keep the larger operand
     // split across the XCDs' L2s
     p->geo.co_major = p->u_code_bytes > (size_t)(n2 * g.T * g.Cin);
-    // fused kernel: 4-wave blocks (taps split 4 ways). WQ8_FUSED_WAVES=16
-    // selects 16-wave blocks (4 taps per wave), kept for comparison: they were
-    // slower on every benchmark layer.
+    // fused kernel, waves per block (the taps are split between them). With
+    // at least three blocks per CU of MI355X (256 CUs), 4-wave blocks keep
+    // every block resident at once (up to five fit a CU); with fewer blocks,
+    // 8-wave blocks (F(6,3) only: 8 taps per wave, all loaded at once) put
+    // more loads in flight per block: 4-10 % faster on the deeper layers,
+    // 2 % slower on the 56 x 56 ResNet-18 layer. WQ8_FUSED_WAVES = 4, 8 or 16
+    // overrides the choice (16 is kept for comparison; it was never faster).
     {
+        const int64_t nblk = ((g.T + 15) / 16) * (int64_t)((g.Cout + 15) / 16);
+        int w = m == 6 && nblk < 3 * 256 ? 8 : 4;
         const char *ov = getenv("WQ8_FUSED_WAVES");
-        p->geo.fused_waves = ov && atoi(ov) == 16 ? 16 : 4;
+        if (ov && (atoi(ov) == 4 || (m == 6 && (atoi(ov) == 8 || atoi(ov) == 16)))) w = atoi(ov);
+        p->geo.fused_waves = w;
     }
     return WQ8_OK;
 }

@@ -272,7 +272,7 @@ def test_fused_output_transform_precision(dev, name):
     assert err <= 2e-5 * r
 
 
-@pytest.mark.parametrize("waves", [4, 16])
+@pytest.mark.parametrize("waves", [4, 8, 16])
 @pytest.mark.parametrize("name,kw", [
     ("c2_f6_n32_c64_56x56_g64", dict(N=2, H=30, W=26, Cin=64, Cout=40)),
     ("c3c_f6_n32_c512_7x7_g64", dict(N=3, H=7, W=7, Cin=192, Cout=24)),
@@ -280,8 +280,8 @@ def test_fused_output_transform_precision(dev, name):
     ("c5_f6_n8_c1280_16x16_g128", dict(N=1, H=9, W=11, Cin=256, Cout=17)),
 ])
 def test_fused_block_shapes(dev, monkeypatch, waves, name, kw):
-    """The fused kernel splits a block's taps over 4 or 16 waves (the plan
-    picks by block count; WQ8_FUSED_WAVES forces one): both shapes give the
+    """The fused kernel splits a block's taps over 4, 8 or 16 waves (the plan
+    picks by block count; WQ8_FUSED_WAVES forces one): every shape gives the
     oracle's result, for one and several quantization groups."""
     monkeypatch.setenv("WQ8_FUSED_WAVES", str(waves))
     L = WL.small(WL.LAYERS[name], **kw)
