@@ -528,116 +528,273 @@ __global__ __launch_bounds__(256) void k_weights(const float *__restrict__ w, in
 }
 
 // ------------------------------------------------------- Hadamard GEMMs
-// Grid (ceil(T/64), ceil(Cout/64), n*n); 4 waves in 2 x 2, each 32 x 32 of
-// (tile, co) as 2 x 2 MFMA 16x16 blocks. Per group: int32 accumulation on
-// MFMA, then M = fma(sV sU, P, M) in group order. KS is the MFMA K-step:
-// 64 (16x16x64) when G is a multiple of 64, else 32 (16x16x32, one per group).
-// MFMA operand layout (16x16xK, int8): lane l holds row (l % 16) of A / column
-// (l % 16) of B, K-slice (l / 16). A and B are loaded with the same K mapping,
-// so the exact int32 dot product does not depend on the order the hardware
-// sums the K slots in. Result: lane l holds rows 4 (l / 16) + i, column l % 16.
-template <int KS, bool I32>
+// Grid (ceil(T/64), ceil(Cout/BC), n*n). A block computes M for 64 tiles x BC
+// output channels of one tap; its 4 waves form 2 x 2, wave (wt, wc) owning
+// tiles 32wt.. and channels (BC/2)wc.. as 2 x BC/32 MFMA 16x16 blocks.
+//
+// K (input channels) runs in chunks of KC bytes (the largest power of two up
+// to 128 dividing Cin). Each chunk's operand rows (64 tile rows of V, BC
+// channel rows of U) and the scales of the groups that end inside it are
+// staged in LDS, double-buffered: while the block computes chunk c, every
+// thread holds chunk c+1 in registers (loaded during chunk c-1) and writes it
+// to the other buffer, then issues the loads of chunk c+2. All global loads
+// are 16-byte pieces of whole rows, so each cache line is fetched once.
+//
+// Per group: the int32 dot products on MFMA (16x16x32 for G <= 32, with zero
+// K slots for G = 16; else G/64 steps of 16x16x64), then
+// M = fma(fl(sV sU), P, M) in group order, so M is bit-identical to the
+// definition. MFMA operand layout (16x16xK, int8): lane l holds row (l % 16)
+// of A / column (l % 16) of B, K-slice (l / 16). A and B use the same K
+// mapping, so the exact int32 dot product does not depend on the order the
+// hardware sums the K slots in. Result: lane l holds rows 4 (l / 16) + i,
+// column l % 16. I32: store each group's int32 products (P) instead of M.
+template <int G, int BC>
+struct S2 {
+    static constexpr int BT = 64, KCM = 128;
+    static constexpr int ROWS = BT + BC;                    // operand rows of a chunk
+    static constexpr int LDR = KCM + 16;                    // LDS row stride in bytes
+    static constexpr int NGM = G < KCM ? KCM / G : 1;       // groups ending in one chunk, at most
+    static constexpr int LPT = ROWS * KCM / 16 / 256;       // 16-byte loads per thread per chunk, at most
+    static constexpr int SPT = (ROWS * NGM + 255) / 256;    // scale loads per thread per chunk, at most
+    static constexpr int NJ = BC / 32;                      // MFMA blocks per wave along the channels
+    static constexpr bool K64 = G >= 64;
+    static_assert(ROWS * KCM / 16 % 256 == 0, "whole loads per thread");
+};
+
+// Where a thread's pieces of chunk c come from and go.
+struct S2Pos {
+    int tap, t0, c0, KC, ppr, npc;
+};
+
+// Groups whose scales chunk c stages: [first, first + count).
+template <int G>
+__device__ __forceinline__ void s2_chunk_groups(int c, int KC, int &first, int &count) {
+    if (G <= KC) {
+        first = c * (KC / G);
+        count = KC / G;
+    } else {
+        first = ((c + 1) * KC) / G - 1;
+        count = ((c + 1) * KC) % G == 0 ? 1 : 0;
+    }
+}
+
+template <int G, int BC, bool I32, int LN, int SN>
+__device__ __forceinline__ void s2_issue(v4i (&ld)[LN], float (&ls)[SN], int c,
+                                         const S2Pos &ps, const Geo &g, __amdgpu_buffer_rsrc_t rV,
+                                         __amdgpu_buffer_rsrc_t rU, __amdgpu_buffer_rsrc_t rsV,
+                                         __amdgpu_buffer_rsrc_t rsU) {
+    using C = S2<G, BC>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < C::LPT; ++j) {
+        const int pce = tid + 256 * j;
+        const int row = pce / ps.ppr, q = pce - row * ps.ppr;
+        int off = kOob;  // reads zero
+        bool u = false;
+        if (pce < ps.npc) {
+            if (row < C::BT) {
+                const int t = ps.t0 + row < g.T ? ps.t0 + row : 0;  // unused rows read row 0
+                off = (ps.tap * (int)g.T + t) * g.Cin + c * ps.KC + 16 * q;
+            } else {
+                const int co = ps.c0 + row - C::BT < g.Cout ? ps.c0 + row - C::BT : 0;
+                off = (ps.tap * g.Cout + co) * g.Cin + c * ps.KC + 16 * q;
+                u = true;
+            }
+        }
+        ld[j] = __builtin_amdgcn_raw_buffer_load_b128(u ? rU : rV, off, 0, 0);
+    }
+    if constexpr (!I32) {
+        int first, count;
+        s2_chunk_groups<G>(c, ps.KC, first, count);
+#pragma unroll
+        for (int j = 0; j < C::SPT; ++j) {
+            const int e = tid + 256 * j;
+            const int row = count ? e / count : 0, k = count ? e - row * count : 0;
+            int off = kOob;
+            bool u = false;
+            if (count && row < C::ROWS) {
+                if (row < C::BT) {
+                    if (ps.t0 + row < g.T) off = ((ps.tap * (int)g.T + ps.t0 + row) * g.ng + first + k) * 4;
+                } else {
+                    if (ps.c0 + row - C::BT < g.Cout)
+                        off = ((ps.tap * g.Cout + ps.c0 + row - C::BT) * g.ng + first + k) * 4;
+                    u = true;
+                }
+            }
+            ls[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(u ? rsU : rsV, off, 0, 0));
+        }
+    }
+}
+
+template <int G, int BC, bool I32, int LN, int SN, int NR>
+__device__ __forceinline__ void s2_commit(const v4i (&ld)[LN], const float (&ls)[SN], int c, const S2Pos &ps,
+                                          int8_t *op, float (*sc)[NR]) {
+    using C = S2<G, BC>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < C::LPT; ++j) {
+        const int pce = tid + 256 * j;
+        const int row = pce / ps.ppr, q = pce - row * ps.ppr;
+        if (pce < ps.npc) *(v4i *)&op[row * C::LDR + 16 * q] = ld[j];
+    }
+    if constexpr (!I32) {
+        int first, count;
+        s2_chunk_groups<G>(c, ps.KC, first, count);
+#pragma unroll
+        for (int j = 0; j < C::SPT; ++j) {
+            const int e = tid + 256 * j;
+            const int row = count ? e / count : 0, k = count ? e - row * count : 0;
+            if (count && row < C::ROWS) sc[k][row] = ls[j];
+        }
+    }
+}
+
+// One group's products are complete: dequantize them into M (or store them)
+// and clear them. k: the group's slot among the chunk's staged scales.
+template <int G, int BC, bool I32, int NJ, int NR>
+__device__ __forceinline__ void s2_finish(v4i (&P)[2][NJ], float (&acc)[2][NJ][4], int gi,
+                                          const float (*sc)[NR], int k, const S2Pos &ps, const Geo &g,
+                                          int32_t *Po) {
+    using C = S2<G, BC>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, kq = lane >> 4, wt = wave & 1, wc = wave >> 1;
+    if constexpr (I32) {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < C::NJ; ++bj) {
+                const int col = ps.c0 + (BC / 2) * wc + 16 * bj + r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = ps.t0 + 32 * wt + 16 * bi + 4 * kq + i;
+                    if (row < g.T && col < g.Cout)
+                        Po[(((size_t)ps.tap * g.ng + gi) * g.T + row) * g.Cout + col] = P[bi][bj][i];
+                }
+            }
+    } else {
+        float su[C::NJ];
+#pragma unroll
+        for (int bj = 0; bj < C::NJ; ++bj) su[bj] = sc[k][C::BT + (BC / 2) * wc + 16 * bj + r];
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+            const float4 sv = *(const float4 *)&sc[k][32 * wt + 16 * bi + 4 * kq];
+            const float svs[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+            for (int bj = 0; bj < C::NJ; ++bj)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[bi][bj][i] = __builtin_fmaf(svs[i] * su[bj], (float)P[bi][bj][i], acc[bi][bj][i]);
+        }
+    }
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < C::NJ; ++bj) P[bi][bj] = v4i{0, 0, 0, 0};
+}
+
+template <int G, int BC, bool I32>
 __global__ __launch_bounds__(256) void k_stage2(const int8_t *__restrict__ Vq,
                                                 const float *__restrict__ sV,
                                                 const int8_t *__restrict__ Uq,
                                                 const float *__restrict__ sU, float *__restrict__ Mo,
-                                                int32_t *__restrict__ Po, Geo g) {
-    const int tap = blockIdx.z;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r = lane & 15, kq = lane >> 4;
-    const int tb = blockIdx.x * 64 + (wave & 1) * 32;
-    const int cb = blockIdx.y * 64 + (wave >> 1) * 32;
-    const int8_t *Vp = Vq + (size_t)tap * g.T * g.Cin;
-    const int8_t *Up = Uq + (size_t)tap * g.Cout * g.Cin;
-    const float *sVp = I32 ? nullptr : sV + (size_t)tap * g.T * g.ng;
-    const float *sUp = I32 ? nullptr : sU + (size_t)tap * g.Cout * g.ng;
+                                                int32_t *__restrict__ Po, Geo g, int KC) {
+    using C = S2<G, BC>;
+    __shared__ __attribute__((aligned(16))) int8_t s_op[2][C::ROWS * C::LDR];
+    __shared__ __attribute__((aligned(16))) float s_sc[2][C::NGM][C::ROWS];
 
-    float acc[2][2][4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, kq = lane >> 4;
+    const int wt = wave & 1, wc = wave >> 1;
+    S2Pos ps;
+    ps.tap = blockIdx.z;
+    ps.t0 = blockIdx.x * C::BT;
+    ps.c0 = blockIdx.y * BC;
+    ps.KC = KC;
+    ps.ppr = KC / 16;            // 16-byte pieces per row
+    ps.npc = C::ROWS * ps.ppr;   // pieces per chunk
+    const int n2 = g.n * g.n;
+    const auto rV = make_rsrc(Vq, (size_t)n2 * g.T * g.Cin);
+    const auto rU = make_rsrc(Uq, (size_t)n2 * g.Cout * g.Cin);
+    const auto rsV = make_rsrc(sV, (size_t)n2 * g.T * g.ng * 4);
+    const auto rsU = make_rsrc(sU, (size_t)n2 * g.Cout * g.ng * 4);
+    const int nch = g.Cin / KC;
+
+    float acc[2][C::NJ][4];
+    v4i P[2][C::NJ];
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
+        for (int bj = 0; bj < C::NJ; ++bj) {
+            P[bi][bj] = v4i{0, 0, 0, 0};
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[bi][bj][i] = 0.0f;
+        }
+    const int arow = (32 * wt + r) * C::LDR, brow = (C::BT + (BC / 2) * wc + r) * C::LDR;
+    const bool kin = C::K64 || 8 * kq < G;
 
-    for (int gi = 0; gi < g.ng; ++gi) {
-        v4i p[2][2];
+    v4i ld[C::LPT];
+    float ls[C::SPT];
+    s2_issue<G, BC, I32>(ld, ls, 0, ps, g, rV, rU, rsV, rsU);
+    s2_commit<G, BC, I32>(ld, ls, 0, ps, s_op[0], s_sc[0]);
+    if (nch > 1) s2_issue<G, BC, I32>(ld, ls, 1, ps, g, rV, rU, rsV, rsU);
+    for (int c = 0; c < nch; ++c) {
+        const int b = c & 1;
+        __syncthreads();  // chunk c is in buffer b; buffer b^1 is free
+        if (c + 1 < nch) {
+            s2_commit<G, BC, I32>(ld, ls, c + 1, ps, s_op[b ^ 1], s_sc[b ^ 1]);
+            if (c + 2 < nch) s2_issue<G, BC, I32>(ld, ls, c + 2, ps, g, rV, rU, rsV, rsU);
+        }
+        const int8_t *sa = &s_op[b][arow];
+        const int8_t *sb = &s_op[b][brow];
+        if constexpr (!C::K64) {
+            // groups of 16 or 32 channels, one 16x16x32 step each
+            const int ngc = KC / G;
+            for (int k = 0; k < ngc; ++k) {
+                const int kb = k * G + (kin ? 8 * kq : 0);
+                long a8[2], b8[C::NJ];
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
+                for (int bi = 0; bi < 2; ++bi) a8[bi] = kin ? *(const long *)&sa[16 * bi * C::LDR + kb] : 0;
 #pragma unroll
-            for (int bj = 0; bj < 2; ++bj) p[bi][bj] = v4i{0, 0, 0, 0};
-        // rows past T / Cout read row 0; their products are never stored
-        if constexpr (KS == 64) {
-            // G is a multiple of 64: G / 64 MFMA K-steps per group
-            for (int k0 = gi * g.G; k0 < (gi + 1) * g.G; k0 += 64) {
-                v4i a[2], b[2];
-#pragma unroll
-                for (int bi = 0; bi < 2; ++bi) {
-                    const int row = tb + 16 * bi + r;
-                    a[bi] = *(const v4i *)(Vp + (size_t)(row < g.T ? row : 0) * g.Cin + k0 + 16 * kq);
-                }
-#pragma unroll
-                for (int bj = 0; bj < 2; ++bj) {
-                    const int col = cb + 16 * bj + r;
-                    b[bj] = *(const v4i *)(Up + (size_t)(col < g.Cout ? col : 0) * g.Cin + k0 + 16 * kq);
-                }
+                for (int bj = 0; bj < C::NJ; ++bj) b8[bj] = kin ? *(const long *)&sb[16 * bj * C::LDR + kb] : 0;
 #pragma unroll
                 for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-                    for (int bj = 0; bj < 2; ++bj)
-                        p[bi][bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[bi], b[bj], p[bi][bj], 0, 0, 0);
+                    for (int bj = 0; bj < C::NJ; ++bj)
+                        P[bi][bj] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a8[bi], b8[bj], P[bi][bj], 0, 0, 0);
+                s2_finish<G, BC, I32>(P, acc, c * ngc + k, s_sc[b], k, ps, g, Po);
             }
         } else {
-            // G = 16 or 32: one K = 32 step per group; K slots past the group are zero
-            const bool kin = 8 * kq < g.G;
-            const int k0 = gi * g.G + (kin ? 8 * kq : 0);
-            long a[2], b[2];
+            // 64-channel steps; a group ends every G / 64 steps
+            const int nst = KC / 64;
+            for (int st = 0; st < nst; ++st) {
+                const int kb = 64 * st + 16 * kq;
+                v4i a[2], bb[C::NJ];
 #pragma unroll
-            for (int bi = 0; bi < 2; ++bi) {
-                const int row = tb + 16 * bi + r;
-                const long v = *(const long *)(Vp + (size_t)(row < g.T ? row : 0) * g.Cin + k0);
-                a[bi] = kin ? v : 0;
+                for (int bi = 0; bi < 2; ++bi) a[bi] = *(const v4i *)&sa[16 * bi * C::LDR + kb];
+#pragma unroll
+                for (int bj = 0; bj < C::NJ; ++bj) bb[bj] = *(const v4i *)&sb[16 * bj * C::LDR + kb];
+#pragma unroll
+                for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < C::NJ; ++bj)
+                        P[bi][bj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[bi], bb[bj], P[bi][bj], 0, 0, 0);
+                const int kend = c * KC + 64 * (st + 1);  // channels done
+                if (kend % G == 0)
+                    s2_finish<G, BC, I32>(P, acc, kend / G - 1, s_sc[b], G <= KC ? (64 * (st + 1)) / G - 1 : 0,
+                                          ps, g, Po);
             }
-#pragma unroll
-            for (int bj = 0; bj < 2; ++bj) {
-                const int col = cb + 16 * bj + r;
-                const long v = *(const long *)(Up + (size_t)(col < g.Cout ? col : 0) * g.Cin + k0);
-                b[bj] = kin ? v : 0;
-            }
-#pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-                for (int bj = 0; bj < 2; ++bj)
-                    p[bi][bj] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[bi], b[bj], p[bi][bj], 0, 0, 0);
         }
-#pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-            for (int bj = 0; bj < 2; ++bj) {
-                const int col = cb + 16 * bj + r;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = tb + 16 * bi + 4 * kq + i;
-                    if (row >= g.T || col >= g.Cout) continue;
-                    if constexpr (I32) {
-                        Po[(((size_t)tap * g.ng + gi) * g.T + row) * g.Cout + col] = p[bi][bj][i];
-                    } else {
-                        const float s = sVp[(size_t)row * g.ng + gi] * sUp[(size_t)col * g.ng + gi];
-                        acc[bi][bj][i] = __builtin_fmaf(s, (float)p[bi][bj][i], acc[bi][bj][i]);
-                    }
-                }
-            }
     }
     if constexpr (!I32) {
-        float *Mp = Mo + (size_t)tap * g.T * g.Cout;
+        float *Mp = Mo + (size_t)ps.tap * g.T * g.Cout;
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-            for (int bj = 0; bj < 2; ++bj) {
-                const int col = cb + 16 * bj + r;
+            for (int bj = 0; bj < C::NJ; ++bj) {
+                const int col = ps.c0 + (BC / 2) * wc + 16 * bj + r;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int row = tb + 16 * bi + 4 * kq + i;
+                    const int row = ps.t0 + 32 * wt + 16 * bi + 4 * kq + i;
                     if (row < g.T && col < g.Cout) Mp[(size_t)row * g.Cout + col] = acc[bi][bj][i];
                 }
             }
@@ -1219,19 +1376,34 @@ wq8_status launch_stage1(const Geo &g, const Mats &mt, wq8_dtype xdt, const void
     return check_launch("input transform");
 }
 
-template <int KS>
-static void stage2_k(const Geo &g, const int8_t *Vq, const float *sV, const int8_t *Uq,
+template <int G, int BC>
+static void stage2_g(const Geo &g, const int8_t *Vq, const float *sV, const int8_t *Uq,
                      const float *sU, float *M, int32_t *P, hipStream_t s) {
-    dim3 grid((unsigned)((g.T + 63) / 64), (g.Cout + 63) / 64, g.n * g.n);
-    if (P) hipLaunchKernelGGL((k_stage2<KS, true>), grid, dim3(256), 0, s, Vq, sV, Uq, sU, M, P, g);
-    else hipLaunchKernelGGL((k_stage2<KS, false>), grid, dim3(256), 0, s, Vq, sV, Uq, sU, M, P, g);
+    int kc = 128;
+    while (g.Cin % kc) kc >>= 1;  // Cin is a multiple of G >= 16
+    dim3 grid((unsigned)((g.T + 63) / 64), (g.Cout + BC - 1) / BC, g.n * g.n);
+    if (P) hipLaunchKernelGGL((k_stage2<G, BC, true>), grid, dim3(256), 0, s, Vq, sV, Uq, sU, M, P, g, kc);
+    else hipLaunchKernelGGL((k_stage2<G, BC, false>), grid, dim3(256), 0, s, Vq, sV, Uq, sU, M, P, g, kc);
+}
+
+template <int G>
+static void stage2_gc(const Geo &g, const int8_t *Vq, const float *sV, const int8_t *Uq,
+                      const float *sU, float *M, int32_t *P, hipStream_t s) {
+    // 128-channel blocks unless that would leave most of a block empty
+    if (g.Cout > 64) stage2_g<G, 128>(g, Vq, sV, Uq, sU, M, P, s);
+    else stage2_g<G, 64>(g, Vq, sV, Uq, sU, M, P, s);
 }
 
 wq8_status launch_stage2(const Geo &g, const int8_t *Vq, const float *sV, const int8_t *Uq,
                          const float *sU, float *M, int32_t *P, void *stream) {
     hipStream_t s = (hipStream_t)stream;
-    if (g.G % 64 == 0) stage2_k<64>(g, Vq, sV, Uq, sU, M, P, s);
-    else stage2_k<32>(g, Vq, sV, Uq, sU, M, P, s);
+    switch (g.G) {
+        case 16: stage2_gc<16>(g, Vq, sV, Uq, sU, M, P, s); break;
+        case 32: stage2_gc<32>(g, Vq, sV, Uq, sU, M, P, s); break;
+        case 64: stage2_gc<64>(g, Vq, sV, Uq, sU, M, P, s); break;
+        case 128: stage2_gc<128>(g, Vq, sV, Uq, sU, M, P, s); break;
+        default: stage2_gc<256>(g, Vq, sV, Uq, sU, M, P, s); break;
+    }
     return check_launch("Hadamard GEMM");
 }
 
