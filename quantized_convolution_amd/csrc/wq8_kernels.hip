@@ -802,56 +802,63 @@ __global__ __launch_bounds__(256) void k_stage2(const int8_t *__restrict__ Vq,
 }
 
 // ------------------------------------------ Y requant + output transform
-// One thread per (tile, co); consecutive threads take consecutive co. ROWS:
-// one Y scale per row of taps, applied to the codes before the transform;
-// otherwise one scale over all taps, applied to the result.
+// A block takes 16 tiles x 16 output channels; thread (ti, ci) = (tid / 16,
+// tid % 16) owns one (tile, co) pair, so M is read 16 channels (64 bytes) at a
+// time. ROWS: one Y scale per row of taps, applied to the codes before the
+// transform; otherwise one scale over all taps, applied to the result. The
+// m x m outputs go through LDS and leave as output rows: consecutive threads
+// write consecutive tiles of one row of one channel.
 template <int M, bool ROWS, typename YT>
 __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT *__restrict__ y,
                                                 int8_t *__restrict__ Yq, float *__restrict__ sY,
                                                 Mats mt, Geo g) {
-    constexpr int N = M + 2, NT = N * N;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (int64_t)g.T * g.Cout) return;
-    const int co = (int)(idx % g.Cout), t = (int)(idx / g.Cout);
+    constexpr int N = M + 2, NT = N * N, MM = M * M;
+    __shared__ float s_out[16][16][MM + 1];  // [ci][ti][pixel]
+    const int tid = threadIdx.x;
+    const int ti = tid >> 4, ci = tid & 15;
+    const int t0 = blockIdx.x * 16, c0 = blockIdx.y * 16;
+    const int t = t0 + ti, co = c0 + ci;
+    const bool ok = t < g.T && co < g.Cout;
     const size_t plane = (size_t)g.T * g.Cout;
+    const size_t idx = (size_t)t * g.Cout + co;
     float mv[NT];
 #pragma unroll
-    for (int tap = 0; tap < NT; ++tap) mv[tap] = Mi[tap * plane + idx];
-    // quantize taps [k0, k0 + len) with one scale
+    for (int tap = 0; tap < NT; ++tap) mv[tap] = ok ? Mi[tap * plane + idx] : 0.0f;
     int q[NT];
-    float yd[NT];  // ROWS: dequantized codes
-    auto quant = [&](int k0, int len) {
+    float yd[NT];
+    float s = 1.0f;
+#pragma unroll
+    for (int blk = 0; blk < (ROWS ? N : 1); ++blk) {
+        // one scale over taps [k0, k0 + len)
+        constexpr int len = ROWS ? N : NT;
+        const int k0 = blk * len;
         float a = 0.0f;
-        for (int k = k0; k < k0 + len; ++k) a = fmaxf(a, fabsf(mv[k]));
-        float s = 0.0f;
+#pragma unroll
+        for (int k = 0; k < len; ++k) a = fmaxf(a, fabsf(mv[k0 + k]));
+        float sc = 0.0f, inv = 0.0f;
         if (a != 0.0f) {
-            const float inv = 127.0f / a;
-            for (int k = k0; k < k0 + len; ++k) q[k] = quant_code(mv[k], inv);
-            s = a / 127.0f;
+            inv = 127.0f / a;
+            sc = a / 127.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < len; ++k) q[k0 + k] = a != 0.0f ? quant_code(mv[k0 + k], inv) : 0;
+        if (ok && sY) sY[ROWS ? idx * N + blk : idx] = sc;
+        if constexpr (ROWS) {
+#pragma unroll
+            for (int k = 0; k < len; ++k) yd[k0 + k] = sc * (float)q[k0 + k];
         } else {
-            for (int k = k0; k < k0 + len; ++k) q[k] = 0;
+            s = sc;
+#pragma unroll
+            for (int k = 0; k < len; ++k) yd[k] = (float)q[k];
         }
-        return s;
-    };
-    float s = 0.0f;
-    if constexpr (ROWS) {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const float si = quant(i * N, N);
-#pragma unroll
-            for (int j = 0; j < N; ++j) yd[i * N + j] = si * (float)q[i * N + j];
-            if (sY) sY[idx * N + i] = si;
-        }
-        s = 1.0f;
-    } else {
-        s = quant(0, NT);
-#pragma unroll
-        for (int k = 0; k < NT; ++k) yd[k] = (float)q[k];
-        if (sY) sY[idx] = s;
     }
-    if (Yq)
+    if (ok && Yq) {
+        uint32_t *yq = (uint32_t *)(Yq + idx * NT);  // NT is a multiple of 4
 #pragma unroll
-        for (int tap = 0; tap < NT; ++tap) Yq[idx * NT + tap] = (int8_t)q[tap];
+        for (int k = 0; k < NT; k += 4)
+            yq[k / 4] = (uint32_t)(q[k] & 255) | (uint32_t)(q[k + 1] & 255) << 8 |
+                        (uint32_t)(q[k + 2] & 255) << 16 | (uint32_t)(q[k + 3] & 255) << 24;
+    }
 
     float z[M][N];
 #pragma unroll
@@ -863,8 +870,6 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
             for (int i = 0; i < N; ++i) acc = __builtin_fmaf(mt.At[aa * N + i], yd[i * N + j], acc);
             z[aa][j] = acc;
         }
-    const int tx = t % g.tW, rr = t / g.tW, ty = rr % g.tH, img = rr / g.tH;
-    YT *yp = y + ((size_t)img * g.Cout + co) * g.Ho * g.Wo;
 #pragma unroll
     for (int aa = 0; aa < M; ++aa)
 #pragma unroll
@@ -872,9 +877,24 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
             float acc = 0.0f;
 #pragma unroll
             for (int j = 0; j < N; ++j) acc = __builtin_fmaf(z[aa][j], mt.At[b * N + j], acc);
-            const int h = ty * M + aa, w = tx * M + b;
-            if (h < g.Ho && w < g.Wo) store_act(yp + (size_t)h * g.Wo + w, ROWS ? acc : acc * s);
+            s_out[ci][ti][aa * M + b] = ROWS ? acc : acc * s;
         }
+    __syncthreads();
+    // rows (ci, ti, aa): 16 * 16 * M of them, consecutive threads on consecutive tiles
+    for (int e = tid; e < 16 * 16 * M; e += 256) {
+        const int eti = e & 15, rest = e >> 4;
+        const int aa = rest % M, eci = rest / M;
+        const int et = t0 + eti, eco = c0 + eci;
+        if (et >= g.T || eco >= g.Cout) continue;
+        const int tx = et % g.tW, rr = et / g.tW, ty = rr % g.tH, img = rr / g.tH;
+        const int h = ty * M + aa;
+        if (h >= g.Ho) continue;
+        YT *yp = y + (((size_t)img * g.Cout + eco) * g.Ho + h) * g.Wo + (size_t)tx * M;
+        const int nb = min(M, g.Wo - tx * M);
+#pragma unroll
+        for (int b = 0; b < M; ++b)
+            if (b < nb) store_act(yp + b, s_out[eci][eti][aa * M + b]);
+    }
 }
 
 // ------------------------------------------------- fused stages 2 + 3
@@ -1410,8 +1430,7 @@ wq8_status launch_stage2(const Geo &g, const int8_t *Vq, const float *sV, const 
 template <int M, typename YT>
 static void stage3_m(const Geo &g, const Mats &mt, const float *Mi, YT *y, int8_t *Yq, float *sY,
                      hipStream_t s) {
-    const int64_t work = (int64_t)g.T * g.Cout;
-    dim3 grid((unsigned)((work + 255) / 256));
+    dim3 grid((unsigned)((g.T + 15) / 16), (g.Cout + 15) / 16);
     if (g.y_rows) hipLaunchKernelGGL((k_stage3<M, true, YT>), grid, dim3(256), 0, s, Mi, y, Yq, sY, mt, g);
     else hipLaunchKernelGGL((k_stage3<M, false, YT>), grid, dim3(256), 0, s, Mi, y, Yq, sY, mt, g);
 }
