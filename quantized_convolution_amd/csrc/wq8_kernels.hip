@@ -554,16 +554,18 @@ struct S2 {
     static constexpr int ROWS = BT + BC;                    // operand rows of a chunk
     static constexpr int LDR = KCM + 16;                    // LDS row stride in bytes
     static constexpr int NGM = G < KCM ? KCM / G : 1;       // groups ending in one chunk, at most
-    static constexpr int LPT = ROWS * KCM / 16 / 256;       // 16-byte loads per thread per chunk, at most
-    static constexpr int SPT = (ROWS * NGM + 255) / 256;    // scale loads per thread per chunk, at most
+    static constexpr int LPT = 2 * (BT * KCM / 16 / 256);   // 16-byte loads per thread per chunk, at most
+    static constexpr int SPT = 2 * ((BT * NGM + 255) / 256); // scale loads per thread per chunk, at most
     static constexpr int NJ = BC / 32;                      // MFMA blocks per wave along the channels
     static constexpr bool K64 = G >= 64;
-    static_assert(ROWS * KCM / 16 % 256 == 0, "whole loads per thread");
+    static_assert(BC == BT && BT * KCM / 16 % 256 == 0, "whole loads per thread and operand");
 };
 
-// Where a thread's pieces of chunk c come from and go.
+// Where a thread's pieces of chunk c come from and go. Rows 0..BT-1 of a
+// chunk are tile rows of V, rows BT.. output-channel rows of U; each row is
+// split into 16-byte pieces (ppr = KC / 16 = 1 << lppr of them).
 struct S2Pos {
-    int tap, t0, c0, KC, ppr, npc;
+    int tap, t0, c0, KC, lppr;
 };
 
 // Groups whose scales chunk c stages: [first, first + count).
@@ -578,50 +580,49 @@ __device__ __forceinline__ void s2_chunk_groups(int c, int KC, int &first, int &
     }
 }
 
+// Loads of one chunk into registers: LPH 16-byte pieces per thread for each
+// of the two operands (a separate loop each, so the buffer resource stays
+// uniform), and the chunk's group scales.
 template <int G, int BC, bool I32, int LN, int SN>
-__device__ __forceinline__ void s2_issue(v4i (&ld)[LN], float (&ls)[SN], int c,
-                                         const S2Pos &ps, const Geo &g, __amdgpu_buffer_rsrc_t rV,
+__device__ __forceinline__ void s2_issue(v4i (&ld)[LN], float (&ls)[SN], int c, const S2Pos &ps,
+                                         const Geo &g, __amdgpu_buffer_rsrc_t rV,
                                          __amdgpu_buffer_rsrc_t rU, __amdgpu_buffer_rsrc_t rsV,
                                          __amdgpu_buffer_rsrc_t rsU) {
     using C = S2<G, BC>;
+    constexpr int LPH = LN / 2;
     const int tid = threadIdx.x;
+    const int npo = C::BT << ps.lppr;  // pieces per operand (BC == BT)
 #pragma unroll
-    for (int j = 0; j < C::LPT; ++j) {
+    for (int j = 0; j < LPH; ++j) {
         const int pce = tid + 256 * j;
-        const int row = pce / ps.ppr, q = pce - row * ps.ppr;
-        int off = kOob;  // reads zero
-        bool u = false;
-        if (pce < ps.npc) {
-            if (row < C::BT) {
-                const int t = ps.t0 + row < g.T ? ps.t0 + row : 0;  // unused rows read row 0
-                off = (ps.tap * (int)g.T + t) * g.Cin + c * ps.KC + 16 * q;
-            } else {
-                const int co = ps.c0 + row - C::BT < g.Cout ? ps.c0 + row - C::BT : 0;
-                off = (ps.tap * g.Cout + co) * g.Cin + c * ps.KC + 16 * q;
-                u = true;
-            }
-        }
-        ld[j] = __builtin_amdgcn_raw_buffer_load_b128(u ? rU : rV, off, 0, 0);
+        const int row = pce >> ps.lppr, q = pce & ((1 << ps.lppr) - 1);
+        const int t = ps.t0 + row < g.T ? ps.t0 + row : 0;  // unused rows read row 0
+        const int off = pce < npo ? (ps.tap * (int)g.T + t) * g.Cin + c * ps.KC + 16 * q : kOob;
+        ld[j] = __builtin_amdgcn_raw_buffer_load_b128(rV, off, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < LPH; ++j) {
+        const int pce = tid + 256 * j;
+        const int row = pce >> ps.lppr, q = pce & ((1 << ps.lppr) - 1);
+        const int co = ps.c0 + row < g.Cout ? ps.c0 + row : 0;
+        const int off = pce < npo ? (ps.tap * g.Cout + co) * g.Cin + c * ps.KC + 16 * q : kOob;
+        ld[LPH + j] = __builtin_amdgcn_raw_buffer_load_b128(rU, off, 0, 0);
     }
     if constexpr (!I32) {
         int first, count;
         s2_chunk_groups<G>(c, ps.KC, first, count);
+        // thread e < count * BT: row e / count, group first + e % count
+        const int lc = count == 8 ? 3 : count == 4 ? 2 : count == 2 ? 1 : 0;
+        constexpr int SPH = SN / 2;
 #pragma unroll
-        for (int j = 0; j < C::SPT; ++j) {
+        for (int j = 0; j < SPH; ++j) {
             const int e = tid + 256 * j;
-            const int row = count ? e / count : 0, k = count ? e - row * count : 0;
-            int off = kOob;
-            bool u = false;
-            if (count && row < C::ROWS) {
-                if (row < C::BT) {
-                    if (ps.t0 + row < g.T) off = ((ps.tap * (int)g.T + ps.t0 + row) * g.ng + first + k) * 4;
-                } else {
-                    if (ps.c0 + row - C::BT < g.Cout)
-                        off = ((ps.tap * g.Cout + ps.c0 + row - C::BT) * g.ng + first + k) * 4;
-                    u = true;
-                }
-            }
-            ls[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(u ? rsU : rsV, off, 0, 0));
+            const int row = e >> lc, k = e & (count - 1);
+            const bool in = count && row < C::BT;
+            const int offv = in && ps.t0 + row < g.T ? ((ps.tap * (int)g.T + ps.t0 + row) * g.ng + first + k) * 4 : kOob;
+            const int offu = in && ps.c0 + row < g.Cout ? ((ps.tap * g.Cout + ps.c0 + row) * g.ng + first + k) * 4 : kOob;
+            ls[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsV, offv, 0, 0));
+            ls[SPH + j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsU, offu, 0, 0));
         }
     }
 }
@@ -630,21 +631,30 @@ template <int G, int BC, bool I32, int LN, int SN, int NR>
 __device__ __forceinline__ void s2_commit(const v4i (&ld)[LN], const float (&ls)[SN], int c, const S2Pos &ps,
                                           int8_t *op, float (*sc)[NR]) {
     using C = S2<G, BC>;
+    constexpr int LPH = LN / 2;
     const int tid = threadIdx.x;
+    const int npo = C::BT << ps.lppr;
 #pragma unroll
-    for (int j = 0; j < C::LPT; ++j) {
-        const int pce = tid + 256 * j;
-        const int row = pce / ps.ppr, q = pce - row * ps.ppr;
-        if (pce < ps.npc) *(v4i *)&op[row * C::LDR + 16 * q] = ld[j];
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < LPH; ++j) {
+            const int pce = tid + 256 * j;
+            const int row = pce >> ps.lppr, q = pce & ((1 << ps.lppr) - 1);
+            if (pce < npo) *(v4i *)&op[(h * C::BT + row) * C::LDR + 16 * q] = ld[h * LPH + j];
+        }
     if constexpr (!I32) {
         int first, count;
         s2_chunk_groups<G>(c, ps.KC, first, count);
+        const int lc = count == 8 ? 3 : count == 4 ? 2 : count == 2 ? 1 : 0;
+        constexpr int SPH = SN / 2;
 #pragma unroll
-        for (int j = 0; j < C::SPT; ++j) {
+        for (int j = 0; j < SPH; ++j) {
             const int e = tid + 256 * j;
-            const int row = count ? e / count : 0, k = count ? e - row * count : 0;
-            if (count && row < C::ROWS) sc[k][row] = ls[j];
+            const int row = e >> lc, k = e & (count - 1);
+            if (count && row < C::BT) {
+                sc[k][row] = ls[j];
+                sc[k][C::BT + row] = ls[SPH + j];
+            }
         }
     }
 }
@@ -710,8 +720,7 @@ __global__ __launch_bounds__(256) void k_stage2(const int8_t *__restrict__ Vq,
     ps.t0 = blockIdx.x * C::BT;
     ps.c0 = blockIdx.y * BC;
     ps.KC = KC;
-    ps.ppr = KC / 16;            // 16-byte pieces per row
-    ps.npc = C::ROWS * ps.ppr;   // pieces per chunk
+    ps.lppr = KC == 128 ? 3 : KC == 64 ? 2 : KC == 32 ? 1 : 0;
     const int n2 = g.n * g.n;
     const auto rV = make_rsrc(Vq, (size_t)n2 * g.T * g.Cin);
     const auto rU = make_rsrc(Uq, (size_t)n2 * g.Cout * g.Cin);
@@ -1396,33 +1405,26 @@ wq8_status launch_stage1(const Geo &g, const Mats &mt, wq8_dtype xdt, const void
     return check_launch("input transform");
 }
 
-template <int G, int BC>
+template <int G>
 static void stage2_g(const Geo &g, const int8_t *Vq, const float *sV, const int8_t *Uq,
                      const float *sU, float *M, int32_t *P, hipStream_t s) {
-    int kc = 128;
+    constexpr int BC = 64;  // 128-channel blocks measured 7-22 % slower on every layer
+    int kc = S2<G, BC>::KCM;
     while (g.Cin % kc) kc >>= 1;  // Cin is a multiple of G >= 16
     dim3 grid((unsigned)((g.T + 63) / 64), (g.Cout + BC - 1) / BC, g.n * g.n);
     if (P) hipLaunchKernelGGL((k_stage2<G, BC, true>), grid, dim3(256), 0, s, Vq, sV, Uq, sU, M, P, g, kc);
     else hipLaunchKernelGGL((k_stage2<G, BC, false>), grid, dim3(256), 0, s, Vq, sV, Uq, sU, M, P, g, kc);
 }
 
-template <int G>
-static void stage2_gc(const Geo &g, const int8_t *Vq, const float *sV, const int8_t *Uq,
-                      const float *sU, float *M, int32_t *P, hipStream_t s) {
-    // 128-channel blocks unless that would leave most of a block empty
-    if (g.Cout > 64) stage2_g<G, 128>(g, Vq, sV, Uq, sU, M, P, s);
-    else stage2_g<G, 64>(g, Vq, sV, Uq, sU, M, P, s);
-}
-
 wq8_status launch_stage2(const Geo &g, const int8_t *Vq, const float *sV, const int8_t *Uq,
                          const float *sU, float *M, int32_t *P, void *stream) {
     hipStream_t s = (hipStream_t)stream;
     switch (g.G) {
-        case 16: stage2_gc<16>(g, Vq, sV, Uq, sU, M, P, s); break;
-        case 32: stage2_gc<32>(g, Vq, sV, Uq, sU, M, P, s); break;
-        case 64: stage2_gc<64>(g, Vq, sV, Uq, sU, M, P, s); break;
-        case 128: stage2_gc<128>(g, Vq, sV, Uq, sU, M, P, s); break;
-        default: stage2_gc<256>(g, Vq, sV, Uq, sU, M, P, s); break;
+        case 16: stage2_g<16>(g, Vq, sV, Uq, sU, M, P, s); break;
+        case 32: stage2_g<32>(g, Vq, sV, Uq, sU, M, P, s); break;
+        case 64: stage2_g<64>(g, Vq, sV, Uq, sU, M, P, s); break;
+        case 128: stage2_g<128>(g, Vq, sV, Uq, sU, M, P, s); break;
+        default: stage2_g<256>(g, Vq, sV, Uq, sU, M, P, s); break;
     }
     return check_launch("Hadamard GEMM");
 }
