@@ -811,9 +811,9 @@ __global__ __launch_bounds__(256) void k_stage2(const int8_t *__restrict__ Vq,
 }
 
 // ------------------------------------------ Y requant + output transform
-// A block takes 16 tiles x 16 output channels; thread (ti, ci) = (tid / 16,
-// tid % 16) owns one (tile, co) pair, so M is read 16 channels (64 bytes) at a
-// time. ROWS: one Y scale per row of taps, applied to the codes before the
+// A block takes 8 tiles x 32 output channels; thread (ti, ci) = (tid / 32,
+// tid % 32) owns one (tile, co) pair, so M is read 32 channels (one 128-byte
+// line) at a time. ROWS: one Y scale per row of taps, applied to the codes before the
 // transform; otherwise one scale over all taps, applied to the result. The
 // m x m outputs go through LDS and leave as output rows: consecutive threads
 // write consecutive tiles of one row of one channel.
@@ -822,17 +822,23 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
                                                 int8_t *__restrict__ Yq, float *__restrict__ sY,
                                                 Mats mt, Geo g) {
     constexpr int N = M + 2, NT = N * N, MM = M * M;
-    __shared__ float s_out[16][16][MM + 1];  // [ci][ti][pixel]
+    constexpr int TI = 8, CI = 32;
+    __shared__ float s_out[CI][TI][MM + 1];  // [ci][ti][pixel]
     const int tid = threadIdx.x;
-    const int ti = tid >> 4, ci = tid & 15;
-    const int t0 = blockIdx.x * 16, c0 = blockIdx.y * 16;
+    const int ti = tid / CI, ci = tid % CI;
+    const int t0 = blockIdx.x * TI, c0 = blockIdx.y * CI;
     const int t = t0 + ti, co = c0 + ci;
     const bool ok = t < g.T && co < g.Cout;
     const size_t plane = (size_t)g.T * g.Cout;
     const size_t idx = (size_t)t * g.Cout + co;
+    // raw buffer loads: no branch per load; pairs outside the layer read zero
+    // (kOob plus a tap plane offset, below 2^31, stays below 2^32)
+    const auto rM = make_rsrc(Mi, (size_t)NT * plane * 4);
+    const int moff = ok ? (int)idx * 4 : kOob;
     float mv[NT];
 #pragma unroll
-    for (int tap = 0; tap < NT; ++tap) mv[tap] = ok ? Mi[tap * plane + idx] : 0.0f;
+    for (int tap = 0; tap < NT; ++tap)
+        mv[tap] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rM, moff, tap * (int)plane * 4, 0));
     int q[NT];
     float yd[NT];
     float s = 1.0f;
@@ -889,9 +895,9 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
             s_out[ci][ti][aa * M + b] = ROWS ? acc : acc * s;
         }
     __syncthreads();
-    // rows (ci, ti, aa): 16 * 16 * M of them, consecutive threads on consecutive tiles
-    for (int e = tid; e < 16 * 16 * M; e += 256) {
-        const int eti = e & 15, rest = e >> 4;
+    // rows (ci, ti, aa): CI * TI * M of them, consecutive threads on consecutive tiles
+    for (int e = tid; e < CI * TI * M; e += 256) {
+        const int eti = e % TI, rest = e / TI;
         const int aa = rest % M, eci = rest / M;
         const int et = t0 + eti, eco = c0 + eci;
         if (et >= g.T || eco >= g.Cout) continue;
@@ -1432,7 +1438,7 @@ wq8_status launch_stage2(const Geo &g, const int8_t *Vq, const float *sV, const 
 template <int M, typename YT>
 static void stage3_m(const Geo &g, const Mats &mt, const float *Mi, YT *y, int8_t *Yq, float *sY,
                      hipStream_t s) {
-    dim3 grid((unsigned)((g.T + 15) / 16), (g.Cout + 15) / 16);
+    dim3 grid((unsigned)((g.T + 7) / 8), (g.Cout + 31) / 32);
     if (g.y_rows) hipLaunchKernelGGL((k_stage3<M, true, YT>), grid, dim3(256), 0, s, Mi, y, Yq, sY, mt, g);
     else hipLaunchKernelGGL((k_stage3<M, false, YT>), grid, dim3(256), 0, s, Mi, y, Yq, sY, mt, g);
 }
