@@ -82,7 +82,7 @@ typedef enum { WQ8_F32 = 0, WQ8_BF16 = 1 } wq8_dtype;
  *           cores with the Kronecker matrix split into two fp16 parts
  *           (fp32 accumulation): outputs within ~1e-5 of their RMS of the
  *           fp32 evaluation;
- *   AUTO:   FUSED when the weight codes are at most 7 MiB, or re-reading
+ *   AUTO:   FUSED when the weight codes are at most 2 MiB, or re-reading
  *           them once per 16-tile block moves fewer bytes than writing and
  *           reading M; else STAGED. */
 typedef enum { WQ8_ALGO_AUTO = 0, WQ8_ALGO_STAGED = 1, WQ8_ALGO_FUSED = 2 } wq8_algo;

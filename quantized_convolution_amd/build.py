@@ -2,7 +2,8 @@
 
 One hipcc invocation compiles the kernels, the host plan and the C ABI into a
 shared library next to this file. Numerics flags: no fp contraction (every fma
-is written out), IEEE fp32 division, fp32 denormals kept.
+is written out), IEEE fp32 division, fp32 denormals kept, no packed fp32
+instructions.
 """
 from __future__ import annotations
 
@@ -22,6 +23,9 @@ FLAGS = [
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the group dequantization reads every
+    # int32 product once, and copies out of AGPRs cost a VALU op each
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

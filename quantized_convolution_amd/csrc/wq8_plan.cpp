@@ -459,12 +459,12 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
     } else if (d->algo == WQ8_ALGO_AUTO) {
         // the fused kernel re-reads the weights once per 16-tile block (from
         // L2 / Infinity Cache when they fit); the staged one writes and reads M.
-        // Up to 7 MiB of weight codes the re-reads stay cheap (measured on
-        // MI355X: fused is 13-27 % faster at 6.5 MB, within 5 % at 4.2 MB, and
-        // staged is clearly faster from 16.8 MB on)
+        // Up to 2 MiB of weight codes the re-reads stay cheap (measured on
+        // MI355X: fused is faster at 0.25 and 1 MiB of codes, staged from
+        // 3.5 MiB on)
         const double reread = (double)p->u_code_bytes * (double)((g.T + 15) / 16);
         const double mbytes = 8.0 * (double)(n2 * g.T * g.Cout);
-        p->fused = p->u_code_bytes <= ((size_t)7 << 20) || reread <= mbytes;
+        p->fused = p->u_code_bytes <= ((size_t)2 << 20) || reread <= mbytes;
     } else {
         p->fused = d->algo == WQ8_ALGO_FUSED;
     }
