@@ -78,6 +78,11 @@ EDGE = [
     WL.small(WL.LAYERS["c5_f6_n8_c1280_16x16_g128"], Cin=256, Cout=40).replace(G=256, name="g256"),
     WL.small(WL.LAYERS["c5_f6_n8_c640_32x32_g32"], Cin=96, Cout=20, H=14, W=14),  # 3 groups
     WL.small(WL.LAYERS["c4_f4_n2_c320_64x64_g64_pert"], N=2, Cin=192, Cout=70, H=21, W=19),
+    # stage-2 K chunks: 8 groups of 16 per 128-byte chunk; 4 groups of 32 per chunk
+    WL.small(WL.LAYERS["c1_f4_n1_c16_16x16_g16"], N=2, H=9, W=11, Cin=128, Cout=72),
+    WL.small(WL.LAYERS["c5_f6_n8_c640_32x32_g32"], Cin=128, Cout=80, H=13, W=14),
+    # 16-byte chunks over three groups of 16; Cout above one 64-channel block
+    WL.small(WL.LAYERS["c1_f4_n1_c16_16x16_g16"], N=1, H=6, W=7, Cin=48, Cout=130),
 ]
 
 
