@@ -33,6 +33,7 @@ struct Geo {
     int fused_waves;          // fused kernel: waves per block (4, 8 or 16)
     int y_rows;               // 1: one Y scale per row of taps (staged only)
     int in_quant;             // wq8_inq: 0 fp32 input transform, 1/2 integer
+    int s1_rows;              // stage-1 window: 0 chosen at launch, 1 all rows, 2 half the rows
 };
 
 // Nonzero patterns of B^T [n][n] and A^T [m][n] for the standard points

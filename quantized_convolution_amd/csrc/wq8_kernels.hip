@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "wq8_device.h"
@@ -195,9 +196,10 @@ __device__ __forceinline__ int reduce_scatter_max(float (&a)[64], int lane) {
 // row; which row and channels is the same for all lanes, so that part of the
 // address, and the zero fill of rows outside the image, go in the scalar
 // offset (a raw buffer load returns zero past the buffer's end).
-template <int M, int G, int TPB_>
+template <int M, int G, int TPB_, bool RH = false>
 struct S1Shape {
     static constexpr int N = M + 2;
+    static constexpr int NR = RH ? N / 2 : N;                // window rows held in LDS at once
     static constexpr int GW = GroupShape<G>::GW;             // waves per tile
     static constexpr int TPB = TPB_;
     static constexpr int NW = TPB * GW;                      // waves per block
@@ -206,16 +208,16 @@ struct S1Shape {
     static constexpr int QPR = NEED <= 8 ? 2 : NEED <= 16 ? 4 : 8;  // quads per window row
     static constexpr int WC = 4 * QPR;
     static constexpr int CPI = 64 / QPR;                     // channels per load instruction
-    static constexpr int CS = N * WC + 1;                    // LDS floats per channel (odd)
-    static constexpr int ITERS = CPB / CPI * N / NW;         // load instructions per wave
-    static_assert(NEED <= WC && ITERS * NW * CPI == CPB * N, "stage-1 window shape");
+    static constexpr int CS = NR * WC + 1;                   // LDS floats per channel (odd)
+    static constexpr int ITERS = CPB / CPI * NR / NW;        // load instructions per wave
+    static_assert(NEED <= WC && ITERS * NW * CPI == CPB * NR, "stage-1 window shape");
     static_assert(16 % CPI == 0, "a load instruction must not straddle a channel group");
 };
 
 // One thread's share of a strip window in flight between load and LDS.
-template <int M, int G, int TPB>
+template <int M, int G, int TPB, bool RH = false>
 struct S1Loads {
-    float f[S1Shape<M, G, TPB>::ITERS][4];
+    float f[S1Shape<M, G, TPB, RH>::ITERS][4];
 };
 
 // A work item's position: image, tile row, first tile column, first channel.
@@ -244,11 +246,12 @@ __device__ __forceinline__ int s1_w0(const S1Item &it, const Geo &g) {
     return ((it.tx0 * M - g.pad) >> 2) << 2;  // arithmetic shift: floor
 }
 
-// Issue all of this thread's window loads for one strip.
-template <int M, int G, int TPB, bool VEC, typename XT>
-__device__ __forceinline__ void s1_issue(S1Loads<M, G, TPB> &ld, __amdgpu_buffer_rsrc_t rx,
-                                         const S1Item &it, const Geo &g, int wave) {
-    using SS = S1Shape<M, G, TPB>;
+// Issue all of this thread's window loads for one strip: window rows
+// r0 .. r0 + NR - 1 of the strip's n input rows.
+template <int M, int G, int TPB, bool VEC, typename XT, bool RH = false>
+__device__ __forceinline__ void s1_issue(S1Loads<M, G, TPB, RH> &ld, __amdgpu_buffer_rsrc_t rx,
+                                         const S1Item &it, const Geo &g, int wave, int r0 = 0) {
+    using SS = S1Shape<M, G, TPB, RH>;
     auto &f = ld.f;
     constexpr int ES = sizeof(XT);
     constexpr int OOB = 0x7ffffff0;  // beyond every buffer the plan accepts; two sum below 2^32
@@ -268,8 +271,8 @@ __device__ __forceinline__ void s1_issue(S1Loads<M, G, TPB> &ld, __amdgpu_buffer
 #pragma unroll
     for (int i = 0; i < SS::ITERS; ++i) {
         const int j = i * SS::NW + wave;  // uniform: window row and channel slice
-        const int row = j % SS::N, cho = (j / SS::N) * SS::CPI;
-        const int h = h0 + row;
+        const int row = j % SS::NR, cho = (j / SS::NR) * SS::CPI;
+        const int h = h0 + r0 + row;
         const int so = h >= 0 && h < g.H && it.c0 + cho < g.Cin ? (cho * hw + h * g.W) * ES : OOB;
         if constexpr (VEC) {
             if constexpr (ES == 4) {
@@ -297,15 +300,15 @@ __device__ __forceinline__ void s1_issue(S1Loads<M, G, TPB> &ld, __amdgpu_buffer
 }
 
 // Write the loaded quads to the LDS window.
-template <int M, int G, int TPB>
-__device__ __forceinline__ void s1_commit(float *win, const S1Loads<M, G, TPB> &ld, int wave) {
-    using SS = S1Shape<M, G, TPB>;
+template <int M, int G, int TPB, bool RH = false>
+__device__ __forceinline__ void s1_commit(float *win, const S1Loads<M, G, TPB, RH> &ld, int wave) {
+    using SS = S1Shape<M, G, TPB, RH>;
     const int lane = threadIdx.x & 63;
     float *lp = win + (lane / SS::QPR) * SS::CS + 4 * (lane % SS::QPR);
 #pragma unroll
     for (int i = 0; i < SS::ITERS; ++i) {
         const int j = i * SS::NW + wave;
-        const int row = j % SS::N, cho = (j / SS::N) * SS::CPI;
+        const int row = j % SS::NR, cho = (j / SS::NR) * SS::CPI;
         float *p = lp + cho * SS::CS + row * SS::WC;
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] = ld.f[i][e];
@@ -317,12 +320,19 @@ __device__ __forceinline__ void s1_commit(float *win, const S1Loads<M, G, TPB> &
 // (mt.Bq) in exact int32 arithmetic (24-bit multiplies: |codes| <= 127 and
 // the first pass stays below n * 127^2 < 2^23), and
 // V = float(Wi) * ((sq_i * sq_j) * sx) goes on to the same V quantization.
-template <int M, int G, int TPB, uint64_t BMASK, bool VEC, typename XT, bool IQ>
-__global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW)) void k_stage1(
+// RH (fp32 input stage only): the LDS window holds half of the n input rows
+// at a time. Both halves' loads are issued at once; the first pass of the
+// transform (B^T d, an fma chain over rows in index order) runs over the
+// first half, the second half then replaces it in LDS and the chains
+// continue, so the sums are unchanged. Half the LDS lets twice as many
+// blocks be resident.
+template <int M, int G, int TPB, uint64_t BMASK, bool VEC, typename XT, bool IQ, bool RH>
+__global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW), RH ? 4 : 1) void k_stage1(
     const XT *__restrict__ x, int8_t *__restrict__ Vq, float *__restrict__ sV, Mats mt, Geo g) {
+    static_assert(!(RH && IQ), "the integer input stage needs the whole patch at once");
     constexpr int N = M + 2, NT = N * N;
     using S = GroupShape<G>;
-    using SS = S1Shape<M, G, TPB>;
+    using SS = S1Shape<M, G, TPB, RH>;
     constexpr int KF = 64 / S::SEG;  // taps per lane after the reduce-scatter
     __shared__ float win[SS::CPB * SS::CS];
     __shared__ float red[S::GW > 1 ? SS::NW : 1][64];
@@ -340,26 +350,64 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW)) void k_stage1(
     const auto rs = make_rsrc(sV, (size_t)n2 * splane * 4);
 
     const S1Item cur = s1_item<M, G, TPB>(xcd_block(blockIdx.x, gridDim.x), g);
-    {
-        S1Loads<M, G, TPB> f;
-        s1_issue<M, G, TPB, VEC, XT>(f, rx, cur, g, wave);
-        s1_commit<M, G, TPB>(win, f, wave);
-    }
+    S1Loads<M, G, TPB, RH> f;
+    s1_issue<M, G, TPB, VEC, XT, RH>(f, rx, cur, g, wave);
+    [[maybe_unused]] S1Loads<M, G, TPB, RH> f2;  // RH: the second half of the rows
+    if constexpr (RH) s1_issue<M, G, TPB, VEC, XT, RH>(f2, rx, cur, g, wave, SS::NR);
+    s1_commit<M, G, TPB, RH>(win, f, wave);
     __syncthreads();
     {
         const int c = cur.c0 + cl, tx = cur.tx0 + tl;
         const bool ok = c < g.Cin && tx < g.tW;
         const int t = (cur.img * g.tH + cur.ty) * g.tW + tx;
-        float d[N][N];
-        {
-            const float *src = win + cl * SS::CS + (cur.tx0 * M - g.pad - s1_w0<M>(cur, g)) + tl * M;
-#pragma unroll
-            for (int k = 0; k < N; ++k)
-#pragma unroll
-                for (int l = 0; l < N; ++l) d[k][l] = src[k * SS::WC + l];
-        }
-
+        const float *src = win + cl * SS::CS + (cur.tx0 * M - g.pad - s1_w0<M>(cur, g)) + tl * M;
         float v[NT];
+        if constexpr (RH) {
+            float t1[N][N];
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+#pragma unroll
+                for (int l = 0; l < N; ++l) t1[i][l] = 0.0f;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                if (hh == 1) {
+                    __syncthreads();  // every wave has read the first half
+                    s1_commit<M, G, TPB, RH>(win, f2, wave);
+                    __syncthreads();
+                }
+                float d[SS::NR][N];
+#pragma unroll
+                for (int k = 0; k < SS::NR; ++k)
+#pragma unroll
+                    for (int l = 0; l < N; ++l) d[k][l] = src[k * SS::WC + l];
+#pragma unroll
+                for (int i = 0; i < N; ++i)
+#pragma unroll
+                    for (int l = 0; l < N; ++l)
+#pragma unroll
+                        for (int kk = 0; kk < SS::NR; ++kk) {
+                            const int k = hh * SS::NR + kk;
+                            if ((BMASK >> (i * N + k)) & 1)
+                                t1[i][l] = __builtin_fmaf(mt.Bt[i * N + k], d[kk][l], t1[i][l]);
+                        }
+            }
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+#pragma unroll
+                for (int j = 0; j < N; ++j) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int l = 0; l < N; ++l)
+                        if ((BMASK >> (j * N + l)) & 1) acc = __builtin_fmaf(t1[i][l], mt.Bt[j * N + l], acc);
+                    v[i * N + j] = acc;
+                }
+        } else {
+        float d[N][N];
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+#pragma unroll
+            for (int l = 0; l < N; ++l) d[k][l] = src[k * SS::WC + l];
+
         if constexpr (IQ) {
             float ax = 0.0f;
 #pragma unroll
@@ -428,6 +476,7 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW)) void k_stage1(
                         if ((BMASK >> (j * N + l)) & 1) acc = __builtin_fmaf(t1[i][l], mt.Bt[j * N + l], acc);
                     v[i * N + j] = acc;
                 }
+        }
         }
         // |v| is taken inside the first reduction step
         float a[64];
@@ -1354,26 +1403,61 @@ wq8_status launch_weights(const Geo &g, const Mats &mt, const float *w, int8_t *
     return check_launch("weight transform");
 }
 
-template <int M, int G, int TPB, uint64_t BMASK, typename XT, bool IQ>
+// Compute units of the current device (queried once per device).
+static int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+template <int M, int G, int TPB, uint64_t BMASK, typename XT, bool IQ, bool RH>
 static void stage1_launch_q(const Geo &g, const Mats &mt, const XT *x, int8_t *Vq, float *sV,
                             hipStream_t s) {
-    using SS = S1Shape<M, G, TPB>;
+    using SS = S1Shape<M, G, TPB, RH>;
     const int nstrip = (g.tW + TPB - 1) / TPB;
     const int chunks = (g.Cin + SS::CPB - 1) / SS::CPB;
     const unsigned blocks = (unsigned)(nstrip * g.N * g.tH * chunks);
     if (g.W % 4 == 0)
-        hipLaunchKernelGGL((k_stage1<M, G, TPB, BMASK, true, XT, IQ>), dim3(blocks), dim3(64 * SS::NW), 0,
+        hipLaunchKernelGGL((k_stage1<M, G, TPB, BMASK, true, XT, IQ, RH>), dim3(blocks), dim3(64 * SS::NW), 0,
                            s, x, Vq, sV, mt, g);
     else
-        hipLaunchKernelGGL((k_stage1<M, G, TPB, BMASK, false, XT, IQ>), dim3(blocks), dim3(64 * SS::NW),
+        hipLaunchKernelGGL((k_stage1<M, G, TPB, BMASK, false, XT, IQ, RH>), dim3(blocks), dim3(64 * SS::NW),
                            0, s, x, Vq, sV, mt, g);
 }
 
 template <int M, int G, int TPB, uint64_t BMASK, typename XT>
 static void stage1_launch(const Geo &g, const Mats &mt, const XT *x, int8_t *Vq, float *sV,
                           hipStream_t s) {
-    if (g.in_quant) stage1_launch_q<M, G, TPB, BMASK, XT, true>(g, mt, x, Vq, sV, s);
-    else stage1_launch_q<M, G, TPB, BMASK, XT, false>(g, mt, x, Vq, sV, s);
+    if (g.in_quant) {
+        stage1_launch_q<M, G, TPB, BMASK, XT, true, false>(g, mt, x, Vq, sV, s);
+        return;
+    }
+    // half-row windows when the strips outnumber the blocks that full
+    // windows let the GPU hold at once (one generation instead of two)
+    bool rh = g.s1_rows == 2;
+    if (g.s1_rows == 0) {
+        static int per_cu = -1;  // resident full-window blocks per CU, this instantiation
+        if (per_cu < 0) {
+            int n = 0;
+            using SS = S1Shape<M, G, TPB>;
+            const auto k = (g.W % 4 == 0) ? k_stage1<M, G, TPB, BMASK, true, XT, false, false>
+                                          : k_stage1<M, G, TPB, BMASK, false, XT, false, false>;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 64 * SS::NW, 0) != hipSuccess) n = 0;
+            per_cu = n;
+        }
+        using SS = S1Shape<M, G, TPB>;
+        const int64_t nblk = (int64_t)((g.tW + TPB - 1) / TPB) * g.N * g.tH * ((g.Cin + SS::CPB - 1) / SS::CPB);
+        rh = per_cu > 0 && nblk > (int64_t)per_cu * device_cus();
+    }
+    if (rh) stage1_launch_q<M, G, TPB, BMASK, XT, false, true>(g, mt, x, Vq, sV, s);
+    else stage1_launch_q<M, G, TPB, BMASK, XT, false, false>(g, mt, x, Vq, sV, s);
 }
 
 template <int M, int G, typename XT>

@@ -495,6 +495,13 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
         if (ov && (atoi(ov) == 4 || (m == 6 && (atoi(ov) == 8 || atoi(ov) == 16)))) w = atoi(ov);
         p->geo.fused_waves = w;
     }
+    // stage-1 window rows: WQ8_STAGE1_ROWS = full or half forces a form (for
+    // tests); otherwise the launch picks half-row windows when the strips
+    // outnumber the blocks full windows let the GPU hold at once
+    {
+        const char *ov = getenv("WQ8_STAGE1_ROWS");
+        p->geo.s1_rows = ov && strcmp(ov, "full") == 0 ? 1 : ov && strcmp(ov, "half") == 0 ? 2 : 0;
+    }
     return WQ8_OK;
 }
 

@@ -277,6 +277,31 @@ def test_fused_output_transform_precision(dev, name):
     assert err <= 2e-5 * r
 
 
+@pytest.mark.parametrize("rows", ["full", "half"])
+@pytest.mark.parametrize("L", [
+    WL.small(WL.LAYERS[WL.BENCH_LAYER], N=2, H=13, W=30, Cin=128, Cout=8),
+    WL.small(WL.LAYERS[WL.BENCH_LAYER], N=1, H=9, W=17, Cin=64, Cout=8).replace(pad=2, name="pad2w17"),
+    WL.small(WL.LAYERS["c4_f4_n2_c320_64x64_g64_pert"], N=1, H=11, W=21, Cin=64, Cout=8),
+    WL.small(WL.LAYERS["c1_f4_n1_c16_16x16_g16"], N=2, H=9, W=11, Cin=48, Cout=8),
+    WL.small(WL.LAYERS["c5_f6_n8_c640_32x32_g128"], N=1, H=10, W=12, Cin=256, Cout=8),
+    WL.small(WL.LAYERS["c5_f6_n8_c640_32x32_g32"], N=1, H=7, W=26, Cin=96, Cout=8),
+], ids=lambda L: L.name)
+def test_stage1_window_rows(dev, monkeypatch, rows, L):
+    """Stage 1 holds all n window rows in LDS, or half of them at a time
+    (the launch picks by how many strips the GPU can hold; WQ8_STAGE1_ROWS
+    forces one): both give the oracle's codes and scales bit for bit."""
+    monkeypatch.setenv("WQ8_STAGE1_ROWS", rows)
+    print(f"\n[case] stage-1 {rows} rows {L.name}", flush=True)
+    d = WL.make(L)
+    from oracle import transforms as T
+    Bt = T.transforms_f32(L.m, list(d["points"]), d["s_b"], d["s_g"])[0]
+    oVq, osV = oracle.stage1(L.m, d["x"], L.pad, L.G, Bt)
+    plan = make_plan(L, d)
+    Vq, sV = q.wq8_stage1(plan, to_dev(d["x"], dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(Vq.cpu().numpy(), oVq) and np.array_equal(sV.cpu().numpy(), osV)
+
+
 @pytest.mark.parametrize("waves", [4, 8, 16])
 @pytest.mark.parametrize("name,kw", [
     ("c2_f6_n32_c64_56x56_g64", dict(N=2, H=30, W=26, Cin=64, Cout=40)),
