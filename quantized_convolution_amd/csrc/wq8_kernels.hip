@@ -4,11 +4,14 @@
 //   k_stage1   V = B^T d B, per-group int8 (input transform)
 //   k_stage2   n*n int8 GEMMs over input channels on MFMA, group dequant
 //   k_stage3   Y requant over the n*n taps of a (tile, co), A^T Yq A, crop
+//   k_fused23  stages 2 and 3 in one kernel, M kept on chip
 //
 // Numerics follow the library contract bit for bit: every transform sum is an
 // fp32 fma chain in index order starting from +0, the quantizer divides with
 // IEEE fp32 division and rounds with rint (ties to even). Build with
-// -ffp-contract=off so nothing else is fused.
+// -ffp-contract=off so nothing else is fused. The one exception is the fused
+// kernel's output transform (fp16 matrix cores on split factors, ~1e-6 of the
+// output RMS from the fp32 chain); its codes and scales are still exact.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
