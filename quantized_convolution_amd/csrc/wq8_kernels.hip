@@ -1410,11 +1410,16 @@ wq8_status launch_weights(const Geo &g, const Mats &mt, const float *w, int8_t *
 static int device_cus() {
     static std::atomic<int> cache[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
     int n = cache[dev].load(std::memory_order_relaxed);
     if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
             n = 256;
+        }
         cache[dev].store(n, std::memory_order_relaxed);
     }
     return n;
@@ -1446,14 +1451,20 @@ static void stage1_launch(const Geo &g, const Mats &mt, const XT *x, int8_t *Vq,
     // windows let the GPU hold at once (one generation instead of two)
     bool rh = g.s1_rows == 2;
     if (g.s1_rows == 0) {
-        static int per_cu = -1;  // resident full-window blocks per CU, this instantiation
+        // resident full-window blocks per CU for this instantiation (both load
+        // forms use the same LDS and nearly the same registers)
+        static std::atomic<int> per_cu_cache{-1};
+        int per_cu = per_cu_cache.load(std::memory_order_relaxed);
         if (per_cu < 0) {
             int n = 0;
             using SS = S1Shape<M, G, TPB>;
-            const auto k = (g.W % 4 == 0) ? k_stage1<M, G, TPB, BMASK, true, XT, false, false>
-                                          : k_stage1<M, G, TPB, BMASK, false, XT, false, false>;
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 64 * SS::NW, 0) != hipSuccess) n = 0;
+            const auto k = k_stage1<M, G, TPB, BMASK, true, XT, false, false>;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 64 * SS::NW, 0) != hipSuccess) {
+                n = 0;                 // full windows; the failed query must not
+                (void)hipGetLastError();  // surface as a launch error
+            }
             per_cu = n;
+            per_cu_cache.store(n, std::memory_order_relaxed);
         }
         using SS = S1Shape<M, G, TPB>;
         const int64_t nblk = (int64_t)((g.tW + TPB - 1) / TPB) * g.N * g.tH * ((g.Cin + SS::CPB - 1) / SS::CPB);
