@@ -361,7 +361,13 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW), RH ? 4 : 1) void k_s
     __syncthreads();
     {
         const int c = cur.c0 + cl, tx = cur.tx0 + tl;
-        const bool ok = c < g.Cin && tx < g.tW;
+        // A wave whose tile lies past the end of the tile row (the strip's
+        // last slots) only helps load the window and meets the barriers.
+        // (With the integer input stage and groups over several waves the
+        // transform holds a barrier, so there every wave runs it.)
+        const bool act = tx < g.tW;
+        const bool skip = !act && !(IQ && S::GW > 1);
+        const bool ok = c < g.Cin && act;
         const int t = (cur.img * g.tH + cur.ty) * g.tW + tx;
         const float *src = win + cl * SS::CS + (cur.tx0 * M - g.pad - s1_w0<M>(cur, g)) + tl * M;
         float v[NT];
@@ -378,6 +384,7 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW), RH ? 4 : 1) void k_s
                     s1_commit<M, G, TPB, RH>(win, f2, wave);
                     __syncthreads();
                 }
+                if (skip) continue;
                 float d[SS::NR][N];
 #pragma unroll
                 for (int k = 0; k < SS::NR; ++k)
@@ -394,6 +401,7 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW), RH ? 4 : 1) void k_s
                                 t1[i][l] = __builtin_fmaf(mt.Bt[i * N + k], d[kk][l], t1[i][l]);
                         }
             }
+            if (!skip)
 #pragma unroll
             for (int i = 0; i < N; ++i)
 #pragma unroll
@@ -404,7 +412,7 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW), RH ? 4 : 1) void k_s
                         if ((BMASK >> (j * N + l)) & 1) acc = __builtin_fmaf(t1[i][l], mt.Bt[j * N + l], acc);
                     v[i * N + j] = acc;
                 }
-        } else {
+        } else if (!skip) {
         float d[N][N];
 #pragma unroll
         for (int k = 0; k < N; ++k)
@@ -483,22 +491,29 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW), RH ? 4 : 1) void k_s
         }
         // |v| is taken inside the first reduction step
         float a[64];
+        int base = 0;
+        if (!skip) {
 #pragma unroll
-        for (int i = 0; i < 64; ++i) a[i] = i < NT ? v[i] : 0.0f;
-        const int base = reduce_scatter_max<S::SEG>(a, lane);
+            for (int i = 0; i < 64; ++i) a[i] = i < NT ? v[i] : 0.0f;
+            base = reduce_scatter_max<S::SEG>(a, lane);
+        }
         if constexpr (S::GW > 1) {
+            // the waves of one group share act, so they skip together
+            if (!skip)
 #pragma unroll
-            for (int j = 0; j < KF; ++j) red[wave][base + j] = a[j];
+                for (int j = 0; j < KF; ++j) red[wave][base + j] = a[j];
             __syncthreads();
             const int w0 = (wave / S::GW) * S::GW;
+            if (!skip)
 #pragma unroll
-            for (int j = 0; j < KF; ++j) {
-                float m = red[w0][base + j];
+                for (int j = 0; j < KF; ++j) {
+                    float m = red[w0][base + j];
 #pragma unroll
-                for (int k = 1; k < S::GW; ++k) m = fmaxf(m, red[w0 + k][base + j]);
-                a[j] = m;
-            }
+                    for (int k = 1; k < S::GW; ++k) m = fmaxf(m, red[w0 + k][base + j]);
+                    a[j] = m;
+                }
         }
+        if (!skip)
 #pragma unroll
         for (int j = 0; j < KF; ++j) {
             const int tap = base + j;
@@ -994,7 +1009,6 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
 // LDS stays below 40 KB and registers below 128 so that four blocks share a
 // CU: on the ResNet-18 layer all 800 blocks then run in a single wave of
 // residency instead of 768 plus a tail of 32.
-constexpr int kCodeBias = 128;
 constexpr float kBiasedMagic = 12583040.0f;  // 1.5 * 2^23 + 128 (even)
 
 // Code rows: 64 bytes per pair; 8-byte chunk c of pair p at c ^ ((p >> 2) & 7).
