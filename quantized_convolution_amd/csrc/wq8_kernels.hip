@@ -109,29 +109,31 @@ __device__ __forceinline__ void quantize_store(const float (&v)[NT], bool ok, in
 //      complement (|x| <= 127 (1 + 2^-24)^2 < 127.5, so the clamp to +-127
 //      never binds and is omitted).
 
+// The group maxima are taken on bit patterns of |v|: non-negative floats
+// order like their unsigned bit patterns, so an integer max gives the float
+// max. (A float max of values that arrive through the integer cross-lane
+// moves would first have to quiet possible signalling NaNs, one more
+// instruction per operand.)
+
 // Reduce-scatter steps: pair a[i] with a[i + K/2]; each lane keeps one half
 // (the max over itself and its partner) and returns 1 if it kept the upper half.
-template <int K, bool ABS = false>
-__device__ __forceinline__ int rs_swap32(float (&a)[64]) {
+template <int K>
+__device__ __forceinline__ int rs_swap32(uint32_t (&a)[64]) {
 #pragma unroll
     for (int i = 0; i < K / 2; ++i) {
-        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[i]), __float_as_uint(a[i + K / 2]),
-                                                  false, false);
-        const float p = __uint_as_float(r[0]), q = __uint_as_float(r[1]);
-        a[i] = ABS ? fmaxf(fabsf(p), fabsf(q)) : fmaxf(p, q);
+        auto r = __builtin_amdgcn_permlane32_swap(a[i], a[i + K / 2], false, false);
+        a[i] = max(r[0], r[1]);
     }
     auto lab = __builtin_amdgcn_permlane32_swap(0u, 1u, false, false);
     return (int)lab[0];
 }
 
-template <int K, bool ABS = false>
-__device__ __forceinline__ int rs_swap16(float (&a)[64]) {
+template <int K>
+__device__ __forceinline__ int rs_swap16(uint32_t (&a)[64]) {
 #pragma unroll
     for (int i = 0; i < K / 2; ++i) {
-        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(a[i + K / 2]),
-                                                  false, false);
-        const float p = __uint_as_float(r[0]), q = __uint_as_float(r[1]);
-        a[i] = ABS ? fmaxf(fabsf(p), fabsf(q)) : fmaxf(p, q);
+        auto r = __builtin_amdgcn_permlane16_swap(a[i], a[i + K / 2], false, false);
+        a[i] = max(r[0], r[1]);
     }
     auto lab = __builtin_amdgcn_permlane16_swap(0u, 1u, false, false);
     return (int)lab[0];
@@ -139,15 +141,16 @@ __device__ __forceinline__ int rs_swap16(float (&a)[64]) {
 
 // DPP exchange with the lane given by CTRL; BIT is a lane-id bit that differs
 // between partners and decides which half a lane keeps.
-template <int K, int CTRL, int BIT, bool ABS = false>
-__device__ __forceinline__ int rs_dpp(float (&a)[64], int lane) {
+template <int K, int CTRL, int BIT>
+__device__ __forceinline__ int rs_dpp(uint32_t (&a)[64], int lane) {
     const bool up = (lane >> BIT) & 1;
 #pragma unroll
     for (int i = 0; i < K / 2; ++i) {
-        const float lo = a[i], hi = a[i + K / 2];
-        const float send = up ? lo : hi, keep = up ? hi : lo;
-        const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xf, 0xf, false));
-        a[i] = ABS ? fmaxf(fabsf(keep), fabsf(recv)) : fmaxf(keep, recv);
+        const uint32_t lo = a[i], hi = a[i + K / 2];
+        const uint32_t send = up ? lo : hi, keep = up ? hi : lo;
+        // old value 0 (the identity of the max) lets the move fold into the max
+        const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, CTRL, 0xf, 0xf, false);
+        a[i] = max(keep, recv);
     }
     return up;
 }
@@ -157,27 +160,28 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppXor7 = 0x141;       // row_half_mirror: lane ^ 7 inside 8 lanes
 constexpr int kDppXor8 = 0x128;       // row_ror:8: lane ^ 8 inside 16 lanes
 
-// Max of |a| over SEG aligned lanes, for 64 values per lane. On return a[j],
-// j < 64/SEG, holds the max for value index base + j (base is returned).
+// Max over SEG aligned lanes, for 64 values per lane (bit patterns of
+// non-negative floats). On return a[j], j < 64/SEG, holds the max for value
+// index base + j (base is returned).
 template <int SEG>
-__device__ __forceinline__ int reduce_scatter_max(float (&a)[64], int lane) {
+__device__ __forceinline__ int reduce_scatter_max(uint32_t (&a)[64], int lane) {
     int base = 0;
     if constexpr (SEG == 64) {
-        base += rs_swap32<64, true>(a) * 32;
+        base += rs_swap32<64>(a) * 32;
         base += rs_swap16<32>(a) * 16;
         base += rs_dpp<16, kDppXor8, 3>(a, lane) * 8;
         base += rs_dpp<8, kDppXor7, 2>(a, lane) * 4;
         base += rs_dpp<4, kDppXor2, 1>(a, lane) * 2;
         base += rs_dpp<2, kDppXor1, 0>(a, lane);
     } else if constexpr (SEG == 32) {
-        base += rs_swap16<64, true>(a) * 32;
+        base += rs_swap16<64>(a) * 32;
         base += rs_dpp<32, kDppXor8, 3>(a, lane) * 16;
         base += rs_dpp<16, kDppXor7, 2>(a, lane) * 8;
         base += rs_dpp<8, kDppXor2, 1>(a, lane) * 4;
         base += rs_dpp<4, kDppXor1, 0>(a, lane) * 2;
     } else {
         static_assert(SEG == 16, "group lanes must be 16, 32 or 64");
-        base += rs_dpp<64, kDppXor8, 3, true>(a, lane) * 32;
+        base += rs_dpp<64, kDppXor8, 3>(a, lane) * 32;
         base += rs_dpp<32, kDppXor7, 2>(a, lane) * 16;
         base += rs_dpp<16, kDppXor2, 1>(a, lane) * 8;
         base += rs_dpp<8, kDppXor1, 0>(a, lane) * 4;
@@ -376,7 +380,8 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW), RH ? 4 : 1) void k_s
 #pragma unroll
             for (int i = 0; i < N; ++i)
 #pragma unroll
-                for (int l = 0; l < N; ++l) t1[i][l] = 0.0f;
+                for (int l = 0; l < N; ++l)
+                    t1[i][l] = (BMASK >> (i * N)) & ((1ull << SS::NR) - 1) ? __builtin_nondeterministic_value(0.0f) : 0.0f;
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 if (hh == 1) {
@@ -397,8 +402,9 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW), RH ? 4 : 1) void k_s
 #pragma unroll
                         for (int kk = 0; kk < SS::NR; ++kk) {
                             const int k = hh * SS::NR + kk;
+                            const bool first = hh == 0 && !((BMASK >> (i * N)) & ((1ull << k) - 1));
                             if ((BMASK >> (i * N + k)) & 1)
-                                t1[i][l] = __builtin_fmaf(mt.Bt[i * N + k], d[kk][l], t1[i][l]);
+                                t1[i][l] = __builtin_fmaf(mt.Bt[i * N + k], d[kk][l], first ? 0.0f : t1[i][l]);
                         }
             }
             if (!skip)
@@ -489,19 +495,19 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW), RH ? 4 : 1) void k_s
                 }
         }
         }
-        // |v| is taken inside the first reduction step
-        float a[64];
+        // bit patterns of |v| (the reduction overwrites them; v is kept)
+        uint32_t a[64];
         int base = 0;
         if (!skip) {
 #pragma unroll
-            for (int i = 0; i < 64; ++i) a[i] = i < NT ? v[i] : 0.0f;
+            for (int i = 0; i < 64; ++i) a[i] = i < NT ? __float_as_uint(v[i]) & 0x7fffffffu : 0u;
             base = reduce_scatter_max<S::SEG>(a, lane);
         }
         if constexpr (S::GW > 1) {
             // the waves of one group share act, so they skip together
             if (!skip)
 #pragma unroll
-                for (int j = 0; j < KF; ++j) red[wave][base + j] = a[j];
+                for (int j = 0; j < KF; ++j) red[wave][base + j] = __uint_as_float(a[j]);
             __syncthreads();
             const int w0 = (wave / S::GW) * S::GW;
             if (!skip)
@@ -510,14 +516,14 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW), RH ? 4 : 1) void k_s
                     float m = red[w0][base + j];
 #pragma unroll
                     for (int k = 1; k < S::GW; ++k) m = fmaxf(m, red[w0 + k][base + j]);
-                    a[j] = m;
+                    a[j] = __float_as_uint(m);
                 }
         }
         if (!skip)
 #pragma unroll
         for (int j = 0; j < KF; ++j) {
             const int tap = base + j;
-            const float am = a[j];
+            const float am = __uint_as_float(a[j]);
             float inv = 0.0f, sc = 0.0f;
             if (am != 0.0f) {
                 inv = 127.0f / am;
