@@ -788,10 +788,16 @@ __global__ __launch_bounds__(256) void k_stage2(const int8_t *__restrict__ Vq,
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, kq = lane >> 4;
     const int wt = wave & 1, wc = wave >> 1;
+    // Block order: tile blocks fastest, then channel blocks, then taps, laid
+    // out so that each XCD runs a contiguous range of it: the tile blocks that
+    // share a slice of U, and all blocks of a tap (which share its V), then
+    // meet in one L2 instead of fetching the same bytes into several.
+    const int ntb = (int)((g.T + C::BT - 1) / C::BT), ncb = (g.Cout + BC - 1) / BC;
+    const int lb = xcd_block(blockIdx.x, gridDim.x);
     S2Pos ps;
-    ps.tap = blockIdx.z;
-    ps.t0 = blockIdx.x * C::BT;
-    ps.c0 = blockIdx.y * BC;
+    ps.tap = lb / (ntb * ncb);
+    ps.t0 = (lb % ntb) * C::BT;
+    ps.c0 = ((lb / ntb) % ncb) * BC;
     ps.KC = KC;
     ps.lppr = KC == 128 ? 3 : KC == 64 ? 2 : KC == 32 ? 1 : 0;
     const int n2 = g.n * g.n;
@@ -1535,7 +1541,9 @@ static void stage2_g(const Geo &g, const int8_t *Vq, const float *sV, const int8
     constexpr int BC = 64;  // 128-channel blocks measured 7-22 % slower on every layer
     int kc = S2<G, BC>::KCM;
     while (g.Cin % kc) kc >>= 1;  // Cin is a multiple of G >= 16
-    dim3 grid((unsigned)((g.T + 63) / 64), (g.Cout + BC - 1) / BC, g.n * g.n);
+    // one dimension: the kernel derives (tile block, channel block, tap)
+    const unsigned nb = (unsigned)((g.T + S2<G, BC>::BT - 1) / S2<G, BC>::BT) * ((g.Cout + BC - 1) / BC) * (g.n * g.n);
+    dim3 grid(nb);
     if (P) hipLaunchKernelGGL((k_stage2<G, BC, true>), grid, dim3(256), 0, s, Vq, sV, Uq, sU, M, P, g, kc);
     else hipLaunchKernelGGL((k_stage2<G, BC, false>), grid, dim3(256), 0, s, Vq, sV, Uq, sU, M, P, g, kc);
 }
