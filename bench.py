@@ -18,6 +18,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -41,8 +42,14 @@ KERNEL_NAMES = {"stage1": "wq8::k_stage1<", "stage2": "wq8::k_stage2<",
 
 
 def kernel_source_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and whitespace are dropped,
+    so only a change to the code itself marks recorded counters stale."""
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def recorded_traffic(layer, kernel):

@@ -94,9 +94,10 @@ __device__ __forceinline__ void quantize_store(const float (&v)[NT], bool ok, in
 
 // ------------------------------------------------------------- stage 1
 // One lane per input channel, one wave per (tile, 64-channel chunk); a block
-// of 4 waves walks tiles in a grid-stride loop. Per tile:
-//   1. load the n x n patch (rows skipped when outside the image; with
-//      W % 4 == 0, three aligned float4 loads per row and a uniform shift);
+// takes one strip of adjacent tiles of a tile row (the work item below). Per
+// tile:
+//   1. the strip's input window is staged in LDS (zero outside the image) and
+//      each lane reads its channel's n x n patch from there;
 //   2. V = B^T d B as fp32 fma chains in index order (terms whose B^T entry is
 //      structurally zero are skipped when the host has verified the pattern;
 //      fma(0, d, acc) == acc, so the chains stay bit-identical);
