@@ -986,6 +986,18 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
         if (h >= g.Ho) continue;
         YT *yp = y + (((size_t)img * g.Cout + eco) * g.Ho + h) * g.Wo + (size_t)tx * M;
         const int nb = min(M, g.Wo - tx * M);
+        if constexpr (sizeof(YT) == 4 && M % 2 == 0) {
+            // fp32 rows of m (even) pixels start at an even element when Wo
+            // is even: pairs of pixels go out as one 8-byte store
+            if (nb == M && g.Wo % 2 == 0) {
+#pragma unroll
+                for (int b = 0; b < M; b += 2) {
+                    const float2 v2 = {s_out[eci][eti][aa * M + b], s_out[eci][eti][aa * M + b + 1]};
+                    *(float2 *)(yp + b) = v2;
+                }
+                continue;
+            }
+        }
 #pragma unroll
         for (int b = 0; b < M; ++b)
             if (b < nb) store_act(yp + b, s_out[eci][eti][aa * M + b]);
