@@ -46,9 +46,15 @@ __device__ __forceinline__ float load_act(const uint16_t *p) {
     return __uint_as_float((uint32_t)(*p) << 16);  // bf16 -> f32, exact
 }
 __device__ __forceinline__ void store_act(float *p, float v) { *p = v; }
-__device__ __forceinline__ void store_act(uint16_t *p, float v) {
-    uint32_t u = __float_as_uint(v);  // f32 -> bf16, nearest even (finite input)
-    *p = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+__device__ __forceinline__ uint16_t to_bf16(float v) {
+    const uint32_t u = __float_as_uint(v);  // f32 -> bf16, nearest even (finite input)
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ void store_act(uint16_t *p, float v) { *p = to_bf16(v); }
+// Two adjacent outputs; p must be aligned to the pair's size.
+__device__ __forceinline__ void store_act2(float *p, float a, float b) { *(float2 *)p = float2{a, b}; }
+__device__ __forceinline__ void store_act2(uint16_t *p, float a, float b) {
+    *(uint32_t *)p = (uint32_t)to_bf16(a) | (uint32_t)to_bf16(b) << 16;
 }
 
 }  // namespace wq8

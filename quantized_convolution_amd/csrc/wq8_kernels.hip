@@ -986,14 +986,15 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
         if (h >= g.Ho) continue;
         YT *yp = y + (((size_t)img * g.Cout + eco) * g.Ho + h) * g.Wo + (size_t)tx * M;
         const int nb = min(M, g.Wo - tx * M);
-        if constexpr (sizeof(YT) == 4 && M % 2 == 0) {
-            // fp32 rows of m (even) pixels start at an even element when Wo
-            // is even: pairs of pixels go out as one 8-byte store
-            if (nb == M && g.Wo % 2 == 0) {
+        if constexpr (M % 2 == 0) {
+            // with m and Wo even a tile's row starts at an even element, so
+            // pairs of pixels go out as one store (8 bytes fp32, 4 bytes bf16)
+            if (g.Wo % 2 == 0) {
 #pragma unroll
                 for (int b = 0; b < M; b += 2) {
-                    const float2 v2 = {s_out[eci][eti][aa * M + b], s_out[eci][eti][aa * M + b + 1]};
-                    *(float2 *)(yp + b) = v2;
+                    const float v0 = s_out[eci][eti][aa * M + b], v1 = s_out[eci][eti][aa * M + b + 1];
+                    if (b + 1 < nb) store_act2(yp + b, v0, v1);
+                    else if (b < nb) store_act(yp + b, v0);
                 }
                 continue;
             }
