@@ -1411,6 +1411,316 @@ __global__ __launch_bounds__(64 * WPB, WPB == 4 && MULTI ? 3 : 4) void k_fused23
     }
 }
 
+// Wide fused block, F(6,3): 32 tiles x 32 output channels (1024 pairs) and
+// 16 waves of NT/16 taps each. Per tap a wave computes the 2 x 2 products of
+// the block's two 16-channel halves of U and two 16-tile halves of V, so each
+// operand byte it loads feeds two MFMAs (the 16 x 16 block loads 2 KB per tap
+// for 256 pairs, this one 4 KB for 1024). Pair p = 32 * (co - co0) + (t - t0);
+// 16 consecutive pairs (one channel, 16 tiles) form an output column block as
+// in k_fused23, and the Y quantization and output transform are those of
+// k_fused23 over 64 column blocks.
+template <int M, int G, bool MULTI, typename YT>
+__global__ __launch_bounds__(1024, 1) void k_fused23w(const int8_t *__restrict__ Vq,
+                                                      const float *__restrict__ sV,
+                                                      const int8_t *__restrict__ Uq,
+                                                      const float *__restrict__ sU, YT *__restrict__ y,
+                                                      Mats mt, Geo g) {
+    constexpr int N = M + 2, NT = N * N, MM = M * M, WPB = 16, NTH = 64 * WPB;
+    constexpr int TPW = NT / WPB;
+    constexpr int NP = 1024;                 // pairs per block
+    constexpr int CBW = NP / 16 / WPB;       // output column blocks per wave
+    constexpr int BS = M == 6 ? 8 : 4;
+    constexpr int RB = M * BS / 16;
+    constexpr bool K64 = G % 64 == 0;
+    constexpr int KSTEPS = K64 ? G / 64 : 1;
+    constexpr int ES = sizeof(YT);
+    constexpr int WLDS = NP * 64 / 4 / WPB;  // floats of the code rows per wave (1024)
+    static_assert(M == 6 && TPW * WPB == NT && TPW == 4, "F(6,3): four taps per wave");
+    static_assert(WLDS >= NP / WPB * WPB && WLDS >= 2 * TPW * 32, "per-wave LDS share");
+    __shared__ __attribute__((aligned(16))) uint8_t codes[NP * 64];
+    __shared__ __attribute__((aligned(16))) _Float16 ktab[2][MM * 64];
+    __shared__ float s_inv[NP], s_out[NP];
+    __shared__ float at_lds[M * N];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    const int nco = (g.Cout + 31) / 32;
+    const int ntb = (int)((g.T + 31) / 32);
+    const int blk = xcd_block(blockIdx.x, gridDim.x);
+    const int cob = g.co_major ? blk / ntb : blk % nco;
+    const int tb = g.co_major ? blk % ntb : blk / nco;
+    const int t0 = tb * 32, co0 = cob * 32;
+    const int tap0 = wave * TPW;
+    const size_t vplane = (size_t)g.T * g.Cin, uplane = (size_t)g.Cout * g.Cin;
+    float *wlds = reinterpret_cast<float *>(codes) + wave * WLDS;
+
+    // ---- K = A^T (x) A^T, scaled, fp16 hi/lo (as in k_fused23)
+    if (tid < M * N) at_lds[tid] = mt.At[tid];
+    __syncthreads();
+    for (int task = tid; task < MM * 8; task += NTH) {
+        const int q = task >> 3, c = task & 7;
+        const int a = q / M, b = q % M;
+        h8 hi, lo;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int tap = 8 * c + u;
+            float kv = 0.0f;
+            if (tap < NT) {
+                const int i = tap / N, j = tap - (tap / N) * N;
+                kv = (at_lds[a * N + i] * mt.kscale) * at_lds[b * N + j];
+            }
+            const _Float16 h = (_Float16)kv;
+            hi[u] = h;
+            lo[u] = (_Float16)(kv - (float)h);
+        }
+        *(h8 *)&ktab[0][kswz(q, c)] = hi;
+        *(h8 *)&ktab[1][kswz(q, c)] = lo;
+    }
+
+    // ---- Hadamard GEMMs: A = U rows co0 + 16 hc + r, B = V rows t0 + 16 ht + r
+    // (rows past Cout or T read row 0: they feed pairs that are never stored)
+    const int n2 = g.n * g.n;
+    const auto rV = make_rsrc(Vq, (size_t)n2 * vplane);
+    const auto rU = make_rsrc(Uq, (size_t)n2 * uplane);
+    const auto rsV = make_rsrc(sV, (size_t)n2 * g.T * g.ng * 4);
+    const auto rsU = make_rsrc(sU, (size_t)n2 * g.Cout * g.ng * 4);
+    const bool kin = K64 || 8 * kq < G;
+    const int koff = K64 ? 16 * kq : (kin ? 8 * kq : 0);
+    int voff[2], uoff[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int tB = t0 + 16 * h + r, coA = co0 + 16 * h + r;
+        voff[h] = (tB < g.T ? tB : 0) * g.Cin + koff;
+        uoff[h] = (coA < g.Cout ? coA : 0) * g.Cin + koff;
+    }
+    float acc[TPW][2][2][4];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int hc = 0; hc < 2; ++hc)
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[j][hc][ht][i] = 0.0f;
+
+    struct TapOps {
+        v4i a[2][K64 ? KSTEPS : 0], b[2][K64 ? KSTEPS : 0];
+        long a8[2], b8[2];
+    };
+    auto load_tap = [&](int j, int gi, TapOps &o) {
+        const int tap = tap0 + j;
+        const int vs = tap * (int)vplane + gi * G, us = tap * (int)uplane + gi * G;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if constexpr (K64) {
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) {
+                    o.a[h][ks] = __builtin_amdgcn_raw_buffer_load_b128(rU, uoff[h], us + ks * 64, 0);
+                    o.b[h][ks] = __builtin_amdgcn_raw_buffer_load_b128(rV, voff[h], vs + ks * 64, 0);
+                }
+            } else {
+                const auto a2 = __builtin_amdgcn_raw_buffer_load_b64(rU, uoff[h], us, 0);
+                const auto b2 = __builtin_amdgcn_raw_buffer_load_b64(rV, voff[h], vs, 0);
+                o.a8[h] = ((long)(uint32_t)a2[1] << 32) | (uint32_t)a2[0];
+                o.b8[h] = ((long)(uint32_t)b2[1] << 32) | (uint32_t)b2[0];
+            }
+        }
+    };
+    // group scales of this wave's taps, staged in its LDS share:
+    // wlds[(s * TPW + j) * 32 + row], s = 0: sV (row = tile), 1: sU (row = channel)
+    constexpr int SL = 2 * TPW * 32 / 64;
+    auto load_scales = [&](int gi, float (&sreg)[SL]) {
+        const int row = lane & 31;
+        const int tr = t0 + row < g.T ? t0 + row : 0, cr = co0 + row < g.Cout ? co0 + row : 0;
+#pragma unroll
+        for (int k = 0; k < SL; ++k) {
+            const int e = 64 * k + lane;
+            const int sw = e / (32 * TPW), j = (e / 32) % TPW;
+            const int tap = tap0 + j;
+            const int off = sw == 0 ? ((tap * (int)g.T + tr) * g.ng + gi) * 4 : ((tap * g.Cout + cr) * g.ng + gi) * 4;
+            sreg[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sw == 0 ? rsV : rsU, off, 0, 0));
+        }
+    };
+    auto put_scales = [&](const float (&sreg)[SL]) {
+#pragma unroll
+        for (int k = 0; k < SL; ++k) wlds[64 * k + lane] = sreg[k];
+    };
+    auto use_tap = [&](int j, const TapOps &o) {
+#pragma unroll
+        for (int hc = 0; hc < 2; ++hc)
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht) {
+                v4i P = v4i{0, 0, 0, 0};
+                if constexpr (K64) {
+#pragma unroll
+                    for (int ks = 0; ks < KSTEPS; ++ks)
+                        P = __builtin_amdgcn_mfma_i32_16x16x64_i8(o.a[hc][ks], o.b[ht][ks], P, 0, 0, 0);
+                } else {
+                    P = __builtin_amdgcn_mfma_i32_16x16x32_i8(kin ? o.a8[hc] : 0, kin ? o.b8[ht] : 0, P, 0, 0, 0);
+                }
+                const float sv = wlds[j * 32 + 16 * ht + r];
+                const float4 su = *(const float4 *)&wlds[(TPW + j) * 32 + 16 * hc + 4 * kq];
+                const float sus[4] = {su.x, su.y, su.z, su.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[j][hc][ht][i] = __builtin_fmaf(sv * sus[i], (float)P[i], acc[j][hc][ht][i]);
+            }
+    };
+    // one tap per batch, the next tap's (or the next group's first tap's)
+    // operands in flight while the current one is computed
+    TapOps buf[2];
+    float snext[SL];
+    load_scales(0, snext);
+    load_tap(0, 0, buf[0]);
+    const int ng = MULTI ? g.ng : 1;
+    for (int gi = 0; gi < ng; ++gi) {
+        put_scales(snext);
+        const int gnext = gi + 1 < ng ? gi + 1 : gi;  // the last group reloads itself (unused)
+        load_scales(gnext, snext);
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int cur = j & 1;
+            if (j + 1 < TPW) load_tap(j + 1, gi, buf[cur ^ 1]);
+            else load_tap(0, gnext, buf[cur ^ 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            use_tap(j, buf[cur]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // ---- Y absmax per pair: this wave's partial maxima in its LDS share
+#pragma unroll
+    for (int hc = 0; hc < 2; ++hc)
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float m = 0.0f;
+#pragma unroll
+                for (int j = 0; j < TPW; ++j) m = fmaxf(m, fabsf(acc[j][hc][ht][i]));
+                wlds[(16 * hc + 4 * kq + i) * 32 + 16 * ht + r] = m;
+            }
+    __syncthreads();
+    {
+        const float *pm = reinterpret_cast<const float *>(codes);
+        float am = pm[tid];
+#pragma unroll
+        for (int w = 1; w < WPB; ++w) am = fmaxf(am, pm[w * WLDS + tid]);
+        float inv = 0.0f, sy = 0.0f;
+        if (am != 0.0f) {
+            inv = 127.0f / am;
+            sy = am / 127.0f;
+        }
+        s_inv[tid] = inv;
+        s_out[tid] = sy * mt.oscale;
+    }
+    __syncthreads();
+    // ---- codes of this wave's four taps, biased bytes, into the pair rows
+#pragma unroll
+    for (int hc = 0; hc < 2; ++hc)
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int p = (16 * hc + 4 * kq + i) * 32 + 16 * ht + r;
+                const float inv = s_inv[p];
+                float yb[TPW];
+#pragma unroll
+                for (int j = 0; j < TPW; ++j) yb[j] = acc[j][hc][ht][i] * inv + kBiasedMagic;
+                *(uint32_t *)&codes[cswz(p, tap0 >> 3) + (tap0 & 7)] = pack4(yb[0], yb[1], yb[2], yb[3]);
+            }
+    __syncthreads();
+
+    // ---- output transform (as in k_fused23): column block cb = wave + 16 c
+    // holds pairs 16 cb .. 16 cb + 15, i.e. channel co0 + cb / 2 and tiles
+    // t0 + 16 (cb % 2) + 0..15; cb % 2 == wave % 2 for all of a wave's blocks
+    const int kg = lane >> 4, nl = lane & 15;
+    h8 bq[CBW][2];
+#pragma unroll
+    for (int c = 0; c < CBW; ++c)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            bq[c][ks] = unbias8(*(const v2i *)&codes[cswz(16 * (wave + WPB * c) + nl, 4 * ks + kg)]);
+    float so[CBW];
+#pragma unroll
+    for (int c = 0; c < CBW; ++c) so[c] = s_out[16 * (wave + WPB * c) + nl];
+
+    const int t = t0 + 16 * (wave & 1) + nl;
+    int ooff[RB], nv[RB];
+    {
+        const int tx = t % g.tW, rr = t / g.tW, ty = rr % g.tH, img = rr / g.tH;
+        const int hv = g.Ho - ty * M, wv = g.Wo - tx * M;
+        const int base = (img * g.Cout * g.Ho + ty * M) * g.Wo + tx * M;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int row0 = 16 * rb + 4 * kg;
+            const int a = row0 / BS, b0 = row0 % BS;
+            const int n = min(4, min(M, wv) - b0);
+            nv[rb] = t < g.T && a < hv && n > 0 ? n : 0;
+            ooff[rb] = (base + a * g.Wo + b0) * ES;
+        }
+    }
+    const auto ry = make_rsrc(y, (size_t)g.N * g.Cout * g.Ho * g.Wo * ES);
+    const int hw = g.Ho * g.Wo;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        h8 ka[2][2];
+        const int prow = 16 * rb + nl, pa = prow / BS, pb = prow % BS;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int part = 0; part < 2; ++part) {
+                if (pb < M) ka[ks][part] = *(const h8 *)&ktab[part][kswz(pa * M + pb, 4 * ks + kg)];
+                else ka[ks][part] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+#pragma unroll
+        for (int cb = 0; cb < CBW; ++cb) {
+            f4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int part = 0; part < 2; ++part)
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[ks][part], bq[cb][ks], d, 0, 0, 0);
+            const int co = co0 + ((wave + WPB * cb) >> 1);
+            if (co < g.Cout) {
+                const int soff = co * hw * ES;
+                const int o = ooff[rb], n = nv[rb];
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = d[i] * so[cb];
+                if constexpr (ES == 4) {
+                    if (n == 4) {
+                        const v4i q = {(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1]),
+                                       (int)__float_as_uint(v[2]), (int)__float_as_uint(v[3])};
+                        __builtin_amdgcn_raw_buffer_store_b128(q, ry, o, soff, 0);
+                    } else {
+                        if (n >= 2) {
+                            const v2i q = {(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1])};
+                            __builtin_amdgcn_raw_buffer_store_b64(q, ry, o, soff, 0);
+                        }
+                        if (n & 1) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[n - 1]), ry, o + 4 * (n - 1), soff, 0);
+                    }
+                } else {
+                    uint32_t hb[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t u = __float_as_uint(v[i]);
+                        hb[i] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+                    }
+                    if (n == 4) {
+                        const v2i q = {(int)(hb[0] | hb[1] << 16), (int)(hb[2] | hb[3] << 16)};
+                        __builtin_amdgcn_raw_buffer_store_b64(q, ry, o, soff, 0);
+                    } else {
+                        if (n >= 2) __builtin_amdgcn_raw_buffer_store_b32(hb[0] | hb[1] << 16, ry, o, soff, 0);
+                        if (n & 1) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hb[n - 1], ry, o + 2 * (n - 1), soff, 0);
+                    }
+                }
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------- launchers
 wq8_status check_launch(const char *what) {
     hipError_t e = hipGetLastError();
@@ -1587,6 +1897,16 @@ template <int M, int G, typename YT>
 static void fused_m_g(const Geo &g, const Mats &mt, const int8_t *Vq, const float *sV,
                       const int8_t *Uq, const float *sU, YT *y, hipStream_t s) {
     const unsigned blocks = (unsigned)(((g.T + 15) / 16) * ((g.Cout + 15) / 16));
+    if constexpr (M == 6 && G <= 64) {
+        if (g.fused_wide) {
+            const unsigned wblocks = (unsigned)(((g.T + 31) / 32) * ((g.Cout + 31) / 32));
+            if (g.ng == 1)
+                hipLaunchKernelGGL((k_fused23w<M, G, false, YT>), dim3(wblocks), dim3(1024), 0, s, Vq, sV, Uq, sU, y, mt, g);
+            else
+                hipLaunchKernelGGL((k_fused23w<M, G, true, YT>), dim3(wblocks), dim3(1024), 0, s, Vq, sV, Uq, sU, y, mt, g);
+            return;
+        }
+    }
     // waves per block as the plan chose (8 or 16 split the taps further; F(4,3)
     // has 36 taps and always uses 4)
     if constexpr (M == 6) {

@@ -494,6 +494,17 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
         const char *ov = getenv("WQ8_FUSED_WAVES");
         if (ov && (atoi(ov) == 4 || (m == 6 && (atoi(ov) == 8 || atoi(ov) == 16)))) w = atoi(ov);
         p->geo.fused_waves = w;
+        // 32 x 32 blocks of 16 waves (F(6,3), G <= 64): each tap's operands
+        // feed four MFMAs, halving the bytes a CU loads for the Hadamard
+        // products. They pay when the 16 x 16 blocks already stack three or
+        // more per CU and the wide blocks all fit at once (one per CU, by
+        // LDS): 18.5 -> 17.3 us on the 56 x 56 ResNet-18 layer; with fewer
+        // blocks they lose 5-90 %. WQ8_FUSED_WIDE = 0 or 1 overrides.
+        const int64_t nwide = ((g.T + 31) / 32) * (int64_t)((g.Cout + 31) / 32);
+        p->geo.fused_wide = m == 6 && d->group <= 64 && nblk >= 3 * 256 && nwide <= 256;
+        const char *wide = getenv("WQ8_FUSED_WIDE");
+        if (wide && (atoi(wide) == 0 || atoi(wide) == 1))
+            p->geo.fused_wide = m == 6 && d->group <= 64 && atoi(wide) == 1;
     }
     // stage-1 window rows: WQ8_STAGE1_ROWS = full or half forces a form (for
     // tests); otherwise the launch picks half-row windows when the strips

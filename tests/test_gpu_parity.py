@@ -326,6 +326,41 @@ def test_fused_block_shapes(dev, monkeypatch, waves, name, kw):
     assert_out(y.cpu().numpy(), ref, f"fused forward, {waves} waves")
 
 
+@pytest.mark.parametrize("name,kw,G,ydt", [
+    # tiles and channels not multiples of 32
+    ("c2_f6_n32_c64_56x56_g64", dict(N=2, H=30, W=26, Cin=64, Cout=40), None, None),
+    # three groups of 32 (the group loop and its cross-group prefetch)
+    ("c5_f6_n8_c640_32x32_g32", dict(N=1, H=13, W=17, Cin=96, Cout=20), None, None),
+    # groups of 16 (half of each K slot is zero), several groups of 64
+    ("c2_f6_n32_c64_56x56_g64", dict(N=1, H=19, W=14, Cin=64, Cout=33), 16, None),
+    ("c3c_f6_n32_c512_7x7_g64", dict(N=3, H=7, W=7, Cin=192, Cout=72), None, None),
+    # bf16 output
+    ("c2_f6_n32_c64_56x56_g64", dict(N=2, H=30, W=26, Cin=64, Cout=40), None, torch.bfloat16),
+])
+def test_fused_wide_blocks(dev, monkeypatch, name, kw, G, ydt):
+    """32 x 32 fused blocks (16 waves, each tap's operands feeding a 2 x 2 of
+    MFMAs): the oracle's result, and bit for bit the output of the 16 x 16
+    blocks, whose per-pair arithmetic they repeat."""
+    L = WL.small(WL.LAYERS[name], **kw)
+    if G is not None:
+        L = L.replace(G=G, name=L.name + f"_g{G}")
+    print(f"\n[case] fused wide {L.name} C={L.Cin}->{L.Cout} {L.H}x{L.W} G={L.G} y={ydt}", flush=True)
+    d = WL.make(L)
+    x, w = to_dev(d["x"], dev), to_dev(d["w"], dev)
+    outs = {}
+    for wide in ("0", "1"):
+        monkeypatch.setenv("WQ8_FUSED_WIDE", wide)
+        plan = make_plan(L, d, ydt=ydt, algo="fused")
+        Uq, sU = q.wq8_weights_prepare(plan, w)
+        outs[wide] = q.wq8_conv_forward(plan, x, Uq, sU)
+        torch.cuda.synchronize()
+    assert torch.equal(outs["0"], outs["1"]), "wide and 16 x 16 fused blocks differ"
+    if ydt is None:
+        ref = oracle.forward(L.m, d["x"], d["w"], L.pad, L.G, points=list(d["points"]), s_b=d["s_b"],
+                             s_g=d["s_g"])
+        assert_out(outs["1"].cpu().numpy(), ref, "fused forward, wide blocks")
+
+
 @pytest.mark.parametrize("name,kw", [
     ("c2_f6_n32_c64_56x56_g64", dict(N=2, H=17, W=23, Cin=64, Cout=24)),
     ("c4_f4_n2_c320_64x64_g64_pert", dict(N=1, H=13, W=9, Cin=128, Cout=20)),
