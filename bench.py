@@ -37,8 +37,9 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POP/s)
 KERNEL_SRC = os.path.join(ROOT, "quantized_convolution_amd", "csrc", "wq8_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # name of each stage's kernel in a rocprofv3 trace (template prefix)
-KERNEL_NAMES = {"stage1": "wq8::k_stage1<", "stage2": "wq8::k_stage2<",
-                "stage3": "wq8::k_stage3<", "stage23": "wq8::k_fused23<"}
+KERNEL_NAMES = {"stage1": ("wq8::k_stage1<",), "stage2": ("wq8::k_stage2<",),
+                "stage3": ("wq8::k_stage3<",),
+                "stage23": ("wq8::k_fused23<", "wq8::k_fused23w<")}
 
 
 def kernel_source_sha():
@@ -67,16 +68,24 @@ def recorded_traffic(layer, kernel):
     return None if k is None else k["bytes_per_launch"]
 
 
+# position of the integer-input-stage flag among k_stage1's template arguments
+# <M, G, TPB, BMASK, VEC, XT, IQ, RH>
+STAGE1_IQ_ARG = 6
+
+
 def stage_of(kernel_name):
     """Stage key of a kernel in a rocprofv3 trace, or None. The stage-1
-    kernel with the integer input stage (last template argument true) is
+    kernel with the integer input stage (template argument IQ true) is
     "stage1_int"."""
-    for stage, prefix in KERNEL_NAMES.items():
-        i = kernel_name.find(prefix)
-        if i >= 0:
-            if stage == "stage1" and kernel_name[i + len(prefix):].split(">")[0].rstrip().endswith("true"):
-                return "stage1_int"
-            return stage
+    for stage, prefixes in KERNEL_NAMES.items():
+        for prefix in prefixes:
+            i = kernel_name.find(prefix)
+            if i >= 0:
+                if stage == "stage1":
+                    args = kernel_name[i + len(prefix):].split(">")[0].split(",")
+                    if len(args) > STAGE1_IQ_ARG and args[STAGE1_IQ_ARG].strip() == "true":
+                        return "stage1_int"
+                return stage
     return None
 
 

@@ -4,7 +4,8 @@
 //   k_stage1   V = B^T d B, per-group int8 (input transform)
 //   k_stage2   n*n int8 GEMMs over input channels on MFMA, group dequant
 //   k_stage3   Y requant over the n*n taps of a (tile, co), A^T Yq A, crop
-//   k_fused23  stages 2 and 3 in one kernel, M kept on chip
+//   k_fused23  stages 2 and 3 in one kernel, M kept on chip (16 x 16 blocks)
+//   k_fused23w the same with 32 x 32 blocks, for F(6,3) layers with many tiles
 //
 // Numerics follow the library contract bit for bit: every transform sum is an
 // fp32 fma chain in index order starting from +0, the quantizer divides with

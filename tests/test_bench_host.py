@@ -36,3 +36,17 @@ def test_recorded_traffic_follows_source_hash():
         got = bench.recorded_traffic(layer, kernel)
         assert got == (v["bytes_per_launch"] if current else None)
     assert bench.recorded_traffic("no_such_layer", "stage1") is None
+
+
+def test_stage_of_reads_the_template_arguments():
+    # k_stage1<M, G, TPB, BMASK, VEC, XT, IQ, RH>: IQ marks the integer input stage
+    s1 = "void wq8::k_stage1<6, 64, 4, 12285395915266489941ul, true, float, {iq}, {rh}>(x)"
+    assert bench.stage_of(s1.format(iq="false", rh="true")) == "stage1"
+    assert bench.stage_of(s1.format(iq="false", rh="false")) == "stage1"
+    assert bench.stage_of(s1.format(iq="true", rh="false")) == "stage1_int"
+    assert bench.stage_of("void wq8::k_stage1<6, 64, 4, 1ul, false, unsigned short, true, false>(x)") == "stage1_int"
+    assert bench.stage_of("void wq8::k_fused23<6, 64, 4, false, float>(a)") == "stage23"
+    assert bench.stage_of("void wq8::k_fused23w<6, 64, false, float>(a)") == "stage23"
+    assert bench.stage_of("void wq8::k_stage2<32, 64, false>(a)") == "stage2"
+    assert bench.stage_of("void wq8::k_stage3<6, false, float>(a)") == "stage3"
+    assert bench.stage_of("void wq8::k_weights<6, 64>(a)") is None
