@@ -1067,6 +1067,140 @@ __device__ __forceinline__ h8 unbias8(v2i w) {
     return r;
 }
 
+// K = A^T (x) A^T (rows a * m + b, taps i * n + j), scaled by the plan's
+// power of two and split into fp16 hi + lo parts, written to LDS by the NTH
+// threads of a block. at_lds holds A^T (m x n) and is visible to them all.
+template <int M, int NTH>
+__device__ __forceinline__ void fused_build_ktab(const float *at_lds, _Float16 (*ktab)[M * M * 64],
+                                                 float kscale) {
+    constexpr int N = M + 2, NT = N * N, MM = M * M;
+    const int tid = threadIdx.x;
+    for (int task = tid; task < MM * 8; task += NTH) {
+        const int q = task >> 3, c = task & 7;
+        const int a = q / M, b = q % M;
+        h8 hi, lo;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int tap = 8 * c + u;
+            float kv = 0.0f;
+            if (tap < NT) {
+                const int i = tap / N, j = tap - (tap / N) * N;
+                kv = (at_lds[a * N + i] * kscale) * at_lds[b * N + j];
+            }
+            const _Float16 h = (_Float16)kv;
+            hi[u] = h;
+            lo[u] = (_Float16)(kv - (float)h);
+        }
+        *(h8 *)&ktab[0][kswz(q, c)] = hi;
+        *(h8 *)&ktab[1][kswz(q, c)] = lo;
+    }
+}
+
+// Output transform and stores of a fused block: D[row][pair] = sum_tap
+// K[row][tap] * Yq[tap][pair] on fp16 MFMA, for this wave's CBW column blocks
+// cb = wave + WPB c (pairs 16 cb .. 16 cb + 15, code rows in LDS). All of a
+// wave's column blocks cover the same 16 tiles, t0w .. t0w + 15 (lane
+// nl = lane % 16 takes tile t0w + nl); column block c is output channel
+// co_base + co_step c. Taps NT..63 of a code row hold stale bytes: finite
+// codes, multiplied by K = 0 there.
+template <int M, int WPB, int CBW, typename YT>
+__device__ __forceinline__ void fused_output(const uint8_t *codes, const _Float16 (*ktab)[M * M * 64],
+                                             const float *s_out, int wave, int t0w, int co_base,
+                                             int co_step, YT *y, const Geo &g) {
+    constexpr int BS = M == 6 ? 8 : 4;  // output row a, column b -> product row a * BS + b
+    constexpr int RB = M * BS / 16;     // 16-row blocks of the output product
+    constexpr int ES = sizeof(YT);
+    const int lane = threadIdx.x & 63;
+    const int kg = lane >> 4, nl = lane & 15;
+    h8 bq[CBW][2];
+#pragma unroll
+    for (int c = 0; c < CBW; ++c)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            bq[c][ks] = unbias8(*(const v2i *)&codes[cswz(16 * (wave + WPB * c) + nl, 4 * ks + kg)]);
+    float so[CBW];
+#pragma unroll
+    for (int c = 0; c < CBW; ++c) so[c] = s_out[16 * (wave + WPB * c) + nl];
+
+    // This lane's tile; per row block, the output pixel (a, b0) of its first
+    // row 16rb + 4kg and how many of its 4 adjacent pixels b0..b0+3 are inside
+    // the image (rows a * BS + b with b >= m are padding).
+    const int t = t0w + nl;
+    int ooff[RB], nv[RB];
+    {
+        const int tx = t % g.tW, rr = t / g.tW, ty = rr % g.tH, img = rr / g.tH;
+        const int hv = g.Ho - ty * M, wv = g.Wo - tx * M;
+        const int base = (img * g.Cout * g.Ho + ty * M) * g.Wo + tx * M;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int row0 = 16 * rb + 4 * kg;
+            const int a = row0 / BS, b0 = row0 % BS;
+            const int n = min(4, min(M, wv) - b0);
+            nv[rb] = t < g.T && a < hv && n > 0 ? n : 0;
+            ooff[rb] = (base + a * g.Wo + b0) * ES;
+        }
+    }
+    const auto ry = make_rsrc(y, (size_t)g.N * g.Cout * g.Ho * g.Wo * ES);
+    const int hw = g.Ho * g.Wo;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        // A fragment: product row 16rb + nl = (a, b); padding rows are zero
+        h8 ka[2][2];
+        const int prow = 16 * rb + nl, pa = prow / BS, pb = prow % BS;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int part = 0; part < 2; ++part) {
+                if (pb < M) ka[ks][part] = *(const h8 *)&ktab[part][kswz(pa * M + pb, 4 * ks + kg)];
+                else ka[ks][part] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+#pragma unroll
+        for (int cb = 0; cb < CBW; ++cb) {
+            f4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int part = 0; part < 2; ++part)
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[ks][part], bq[cb][ks], d, 0, 0, 0);
+            const int co = co_base + co_step * cb;
+            if (co < g.Cout) {
+                const int soff = co * hw * ES;
+                const int o = ooff[rb], n = nv[rb];
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = d[i] * so[cb];
+                if constexpr (ES == 4) {
+                    if (n == 4) {
+                        const v4i q = {(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1]),
+                                       (int)__float_as_uint(v[2]), (int)__float_as_uint(v[3])};
+                        __builtin_amdgcn_raw_buffer_store_b128(q, ry, o, soff, 0);
+                    } else {
+                        if (n >= 2) {
+                            const v2i q = {(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1])};
+                            __builtin_amdgcn_raw_buffer_store_b64(q, ry, o, soff, 0);
+                        }
+                        if (n & 1) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[n - 1]), ry, o + 4 * (n - 1), soff, 0);
+                    }
+                } else {
+                    uint32_t hb[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t u = __float_as_uint(v[i]);
+                        hb[i] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+                    }
+                    if (n == 4) {
+                        const v2i q = {(int)(hb[0] | hb[1] << 16), (int)(hb[2] | hb[3] << 16)};
+                        __builtin_amdgcn_raw_buffer_store_b64(q, ry, o, soff, 0);
+                    } else {
+                        if (n >= 2) __builtin_amdgcn_raw_buffer_store_b32(hb[0] | hb[1] << 16, ry, o, soff, 0);
+                        if (n & 1) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hb[n - 1], ry, o + 2 * (n - 1), soff, 0);
+                    }
+                }
+            }
+        }
+    }
+}
+
 // WPB: waves per block (the block's taps are split evenly between them).
 // MULTI: more than one quantization group along Cin (the group loop runs and
 // prefetches across groups).
@@ -1078,11 +1212,8 @@ __global__ __launch_bounds__(64 * WPB, WPB == 4 && MULTI ? 3 : 4) void k_fused23
                                                  Mats mt, Geo g) {
     constexpr int N = M + 2, NT = N * N, TPW = NT / WPB, MM = M * M, NTH = 64 * WPB;
     constexpr int CBW = 16 / WPB;       // output column blocks (16 pairs) per wave
-    constexpr int BS = M == 6 ? 8 : 4;  // output row a, column b -> product row a * BS + b
-    constexpr int RB = M * BS / 16;     // 16-row blocks of the output product
     constexpr bool K64 = G % 64 == 0;
     constexpr int KSTEPS = K64 ? G / 64 : 1;
-    constexpr int ES = sizeof(YT);
     static_assert(NT <= 64 && TPW * WPB == NT && TPW <= 16 && CBW * WPB == 16, "taps per wave");
     // codes: 256 pairs x 64 bytes; during the Hadamard part each wave uses its
     // share (16 KB / WPB) for one group's scales [2][TPW taps][16 rows], then
@@ -1111,25 +1242,7 @@ __global__ __launch_bounds__(64 * WPB, WPB == 4 && MULTI ? 3 : 4) void k_fused23
     // ---- K = A^T (x) A^T (rows a * m + b, taps i * n + j), scaled, fp16 hi/lo
     if (tid < M * N) at_lds[tid] = mt.At[tid];
     __syncthreads();
-    for (int task = tid; task < MM * 8; task += NTH) {
-        const int q = task >> 3, c = task & 7;
-        const int a = q / M, b = q % M;
-        h8 hi, lo;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int tap = 8 * c + u;
-            float kv = 0.0f;
-            if (tap < NT) {
-                const int i = tap / N, j = tap - (tap / N) * N;
-                kv = (at_lds[a * N + i] * mt.kscale) * at_lds[b * N + j];
-            }
-            const _Float16 h = (_Float16)kv;
-            hi[u] = h;
-            lo[u] = (_Float16)(kv - (float)h);
-        }
-        *(h8 *)&ktab[0][kswz(q, c)] = hi;
-        *(h8 *)&ktab[1][kswz(q, c)] = lo;
-    }
+    fused_build_ktab<M, NTH>(at_lds, ktab, mt.kscale);
 
     // ---- Hadamard GEMMs for this wave's taps
     // Rows past T or Cout read row 0 instead: they only feed (tile, co) pairs
@@ -1317,99 +1430,9 @@ __global__ __launch_bounds__(64 * WPB, WPB == 4 && MULTI ? 3 : 4) void k_fused23
     }
     __syncthreads();
 
-    // ---- output transform: D[row][pair] = sum_tap K[row][tap] * Yq[tap][pair]
-    // Column block cb (pairs 16cb .. 16cb+15 = tiles t0..t0+15 of output
-    // channel co0 + cb) goes to wave cb % WPB. Lane (kg = lane / 16, nl = lane % 16).
-    // Taps NT..63 of a code row hold stale bytes: finite codes, multiplied by
-    // K = 0 there.
-    const int kg = lane >> 4, nl = lane & 15;
-    h8 bq[CBW][2];
-#pragma unroll
-    for (int c = 0; c < CBW; ++c)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            bq[c][ks] = unbias8(*(const v2i *)&codes[cswz(16 * (wave + WPB * c) + nl, 4 * ks + kg)]);
-    float so[CBW];
-#pragma unroll
-    for (int c = 0; c < CBW; ++c) so[c] = s_out[16 * (wave + WPB * c) + nl];
-
-    // This lane's tile; per row block, the output pixel (a, b0) of its first
-    // row 16rb + 4kg and how many of its 4 adjacent pixels b0..b0+3 are inside
-    // the image (rows a * BS + b with b >= m are padding).
-    const int t = t0 + nl;
-    int ooff[RB], nv[RB];
-    {
-        const int tx = t % g.tW, rr = t / g.tW, ty = rr % g.tH, img = rr / g.tH;
-        const int hv = g.Ho - ty * M, wv = g.Wo - tx * M;
-        const int base = (img * g.Cout * g.Ho + ty * M) * g.Wo + tx * M;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const int row0 = 16 * rb + 4 * kg;
-            const int a = row0 / BS, b0 = row0 % BS;
-            const int n = min(4, min(M, wv) - b0);
-            nv[rb] = t < g.T && a < hv && n > 0 ? n : 0;
-            ooff[rb] = (base + a * g.Wo + b0) * ES;
-        }
-    }
-    const auto ry = make_rsrc(y, (size_t)g.N * g.Cout * g.Ho * g.Wo * ES);
-    const int hw = g.Ho * g.Wo;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        // A fragment: product row 16rb + nl = (a, b); padding rows are zero
-        h8 ka[2][2];
-        const int prow = 16 * rb + nl, pa = prow / BS, pb = prow % BS;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int part = 0; part < 2; ++part) {
-                if (pb < M) ka[ks][part] = *(const h8 *)&ktab[part][kswz(pa * M + pb, 4 * ks + kg)];
-                else ka[ks][part] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-#pragma unroll
-        for (int cb = 0; cb < CBW; ++cb) {
-            f4 d = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int part = 0; part < 2; ++part)
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[ks][part], bq[cb][ks], d, 0, 0, 0);
-            const int co = co0 + wave + WPB * cb;
-            if (co < g.Cout) {
-                const int soff = co * hw * ES;
-                const int o = ooff[rb], n = nv[rb];
-                float v[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = d[i] * so[cb];
-                if constexpr (ES == 4) {
-                    if (n == 4) {
-                        const v4i q = {(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1]),
-                                       (int)__float_as_uint(v[2]), (int)__float_as_uint(v[3])};
-                        __builtin_amdgcn_raw_buffer_store_b128(q, ry, o, soff, 0);
-                    } else {
-                        if (n >= 2) {
-                            const v2i q = {(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1])};
-                            __builtin_amdgcn_raw_buffer_store_b64(q, ry, o, soff, 0);
-                        }
-                        if (n & 1) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[n - 1]), ry, o + 4 * (n - 1), soff, 0);
-                    }
-                } else {
-                    uint32_t hb[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t u = __float_as_uint(v[i]);
-                        hb[i] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-                    }
-                    if (n == 4) {
-                        const v2i q = {(int)(hb[0] | hb[1] << 16), (int)(hb[2] | hb[3] << 16)};
-                        __builtin_amdgcn_raw_buffer_store_b64(q, ry, o, soff, 0);
-                    } else {
-                        if (n >= 2) __builtin_amdgcn_raw_buffer_store_b32(hb[0] | hb[1] << 16, ry, o, soff, 0);
-                        if (n & 1) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hb[n - 1], ry, o + 2 * (n - 1), soff, 0);
-                    }
-                }
-            }
-        }
-    }
+    // ---- output transform: column block cb = wave + WPB c holds tiles
+    // t0 .. t0 + 15 of output channel co0 + cb
+    fused_output<M, WPB, CBW, YT>(codes, ktab, s_out, wave, t0, co0 + wave, WPB, y, g);
 }
 
 // Wide fused block, F(6,3): 32 tiles x 32 output channels (1024 pairs) and
@@ -1430,11 +1453,8 @@ __global__ __launch_bounds__(1024, 1) void k_fused23w(const int8_t *__restrict__
     constexpr int TPW = NT / WPB;
     constexpr int NP = 1024;                 // pairs per block
     constexpr int CBW = NP / 16 / WPB;       // output column blocks per wave
-    constexpr int BS = M == 6 ? 8 : 4;
-    constexpr int RB = M * BS / 16;
     constexpr bool K64 = G % 64 == 0;
     constexpr int KSTEPS = K64 ? G / 64 : 1;
-    constexpr int ES = sizeof(YT);
     constexpr int WLDS = NP * 64 / 4 / WPB;  // floats of the code rows per wave (1024)
     static_assert(M == 6 && TPW * WPB == NT && TPW == 4, "F(6,3): four taps per wave");
     static_assert(WLDS >= NP / WPB * WPB && WLDS >= 2 * TPW * 32, "per-wave LDS share");
@@ -1460,25 +1480,7 @@ __global__ __launch_bounds__(1024, 1) void k_fused23w(const int8_t *__restrict__
     // ---- K = A^T (x) A^T, scaled, fp16 hi/lo (as in k_fused23)
     if (tid < M * N) at_lds[tid] = mt.At[tid];
     __syncthreads();
-    for (int task = tid; task < MM * 8; task += NTH) {
-        const int q = task >> 3, c = task & 7;
-        const int a = q / M, b = q % M;
-        h8 hi, lo;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int tap = 8 * c + u;
-            float kv = 0.0f;
-            if (tap < NT) {
-                const int i = tap / N, j = tap - (tap / N) * N;
-                kv = (at_lds[a * N + i] * mt.kscale) * at_lds[b * N + j];
-            }
-            const _Float16 h = (_Float16)kv;
-            hi[u] = h;
-            lo[u] = (_Float16)(kv - (float)h);
-        }
-        *(h8 *)&ktab[0][kswz(q, c)] = hi;
-        *(h8 *)&ktab[1][kswz(q, c)] = lo;
-    }
+    fused_build_ktab<M, NTH>(at_lds, ktab, mt.kscale);
 
     // ---- Hadamard GEMMs: A = U rows co0 + 16 hc + r, B = V rows t0 + 16 ht + r
     // (rows past Cout or T read row 0: they feed pairs that are never stored)
@@ -1633,93 +1635,11 @@ __global__ __launch_bounds__(1024, 1) void k_fused23w(const int8_t *__restrict__
             }
     __syncthreads();
 
-    // ---- output transform (as in k_fused23): column block cb = wave + 16 c
-    // holds pairs 16 cb .. 16 cb + 15, i.e. channel co0 + cb / 2 and tiles
+    // ---- output transform: column block cb = wave + 16 c holds pairs
+    // 16 cb .. 16 cb + 15, i.e. channel co0 + cb / 2 and tiles
     // t0 + 16 (cb % 2) + 0..15; cb % 2 == wave % 2 for all of a wave's blocks
-    const int kg = lane >> 4, nl = lane & 15;
-    h8 bq[CBW][2];
-#pragma unroll
-    for (int c = 0; c < CBW; ++c)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            bq[c][ks] = unbias8(*(const v2i *)&codes[cswz(16 * (wave + WPB * c) + nl, 4 * ks + kg)]);
-    float so[CBW];
-#pragma unroll
-    for (int c = 0; c < CBW; ++c) so[c] = s_out[16 * (wave + WPB * c) + nl];
-
-    const int t = t0 + 16 * (wave & 1) + nl;
-    int ooff[RB], nv[RB];
-    {
-        const int tx = t % g.tW, rr = t / g.tW, ty = rr % g.tH, img = rr / g.tH;
-        const int hv = g.Ho - ty * M, wv = g.Wo - tx * M;
-        const int base = (img * g.Cout * g.Ho + ty * M) * g.Wo + tx * M;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const int row0 = 16 * rb + 4 * kg;
-            const int a = row0 / BS, b0 = row0 % BS;
-            const int n = min(4, min(M, wv) - b0);
-            nv[rb] = t < g.T && a < hv && n > 0 ? n : 0;
-            ooff[rb] = (base + a * g.Wo + b0) * ES;
-        }
-    }
-    const auto ry = make_rsrc(y, (size_t)g.N * g.Cout * g.Ho * g.Wo * ES);
-    const int hw = g.Ho * g.Wo;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        h8 ka[2][2];
-        const int prow = 16 * rb + nl, pa = prow / BS, pb = prow % BS;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int part = 0; part < 2; ++part) {
-                if (pb < M) ka[ks][part] = *(const h8 *)&ktab[part][kswz(pa * M + pb, 4 * ks + kg)];
-                else ka[ks][part] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-#pragma unroll
-        for (int cb = 0; cb < CBW; ++cb) {
-            f4 d = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int part = 0; part < 2; ++part)
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[ks][part], bq[cb][ks], d, 0, 0, 0);
-            const int co = co0 + ((wave + WPB * cb) >> 1);
-            if (co < g.Cout) {
-                const int soff = co * hw * ES;
-                const int o = ooff[rb], n = nv[rb];
-                float v[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = d[i] * so[cb];
-                if constexpr (ES == 4) {
-                    if (n == 4) {
-                        const v4i q = {(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1]),
-                                       (int)__float_as_uint(v[2]), (int)__float_as_uint(v[3])};
-                        __builtin_amdgcn_raw_buffer_store_b128(q, ry, o, soff, 0);
-                    } else {
-                        if (n >= 2) {
-                            const v2i q = {(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1])};
-                            __builtin_amdgcn_raw_buffer_store_b64(q, ry, o, soff, 0);
-                        }
-                        if (n & 1) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[n - 1]), ry, o + 4 * (n - 1), soff, 0);
-                    }
-                } else {
-                    uint32_t hb[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t u = __float_as_uint(v[i]);
-                        hb[i] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-                    }
-                    if (n == 4) {
-                        const v2i q = {(int)(hb[0] | hb[1] << 16), (int)(hb[2] | hb[3] << 16)};
-                        __builtin_amdgcn_raw_buffer_store_b64(q, ry, o, soff, 0);
-                    } else {
-                        if (n >= 2) __builtin_amdgcn_raw_buffer_store_b32(hb[0] | hb[1] << 16, ry, o, soff, 0);
-                        if (n & 1) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hb[n - 1], ry, o + 2 * (n - 1), soff, 0);
-                    }
-                }
-            }
-        }
-    }
+    fused_output<M, WPB, CBW, YT>(codes, ktab, s_out, wave, t0 + 16 * (wave & 1), co0 + (wave >> 1), WPB / 2,
+                                  y, g);
 }
 
 // ------------------------------------------------------------- launchers
