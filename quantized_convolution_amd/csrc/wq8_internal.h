@@ -31,7 +31,7 @@ struct Geo {
     int co_major;             // fused kernel: 1 = output-channel blocks outermost
                               // (weights larger than the activation codes)
     int fused_waves;          // fused kernel: waves per block (4, 8 or 16)
-    int fused_wide;           // fused kernel, F(6,3): 32 x 32 blocks of 16 waves
+    int fused_wide;           // fused kernel, F(6,3): 0 16 x 16 blocks; 1 32 x 32, 2 32 tiles x 16 channels, 3 16 x 32
     int y_rows;               // 1: one Y scale per row of taps (staged only)
     int in_quant;             // wq8_inq: 0 fp32 input transform, 1/2 integer
     int s1_rows;              // stage-1 window: 0 chosen at launch, 1 all rows, 2 half the rows

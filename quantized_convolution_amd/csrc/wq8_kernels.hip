@@ -1435,29 +1435,33 @@ __global__ __launch_bounds__(64 * WPB, WPB == 4 && MULTI ? 3 : 4) void k_fused23
     fused_output<M, WPB, CBW, YT>(codes, ktab, s_out, wave, t0, co0 + wave, WPB, y, g);
 }
 
-// Wide fused block, F(6,3): 32 tiles x 32 output channels (1024 pairs) and
-// 16 waves of NT/16 taps each. Per tap a wave computes the 2 x 2 products of
-// the block's two 16-channel halves of U and two 16-tile halves of V, so each
-// operand byte it loads feeds two MFMAs (the 16 x 16 block loads 2 KB per tap
-// for 256 pairs, this one 4 KB for 1024). Pair p = 32 * (co - co0) + (t - t0);
-// 16 consecutive pairs (one channel, 16 tiles) form an output column block as
-// in k_fused23, and the Y quantization and output transform are those of
-// k_fused23 over 64 column blocks.
-template <int M, int G, bool MULTI, typename YT>
-__global__ __launch_bounds__(1024, 1) void k_fused23w(const int8_t *__restrict__ Vq,
-                                                      const float *__restrict__ sV,
-                                                      const int8_t *__restrict__ Uq,
-                                                      const float *__restrict__ sU, YT *__restrict__ y,
-                                                      Mats mt, Geo g) {
-    constexpr int N = M + 2, NT = N * N, MM = M * M, WPB = 16, NTH = 64 * WPB;
-    constexpr int TPW = NT / WPB;
-    constexpr int NP = 1024;                 // pairs per block
-    constexpr int CBW = NP / 16 / WPB;       // output column blocks per wave
+// Wide fused blocks, F(6,3): HT x 16 tiles by HC x 16 output channels, with
+// (HT, HC) = (2, 2), (2, 1) or (1, 2), and 4 HT HC waves of NT / (4 HT HC)
+// taps each. Per tap a wave computes the HC x HT 16 x 16 products of the
+// block's channel and tile halves, so each operand byte it loads feeds HT or
+// HC MFMAs (a 16 x 16 block loads 2 KB per tap for 256 pairs; a 32 x 32 one
+// 4 KB for 1024). Pair p = 16 HT (co - co0) + (t - t0); 16 consecutive pairs
+// (one channel, 16 tiles) form an output column block as in k_fused23, and
+// the Y quantization and output transform are those of k_fused23 over the
+// block's column blocks, so the output is bit for bit that of k_fused23.
+template <int M, int G, int HT, int HC, bool MULTI, typename YT>
+__global__ __launch_bounds__(256 * HT * HC, 1) void k_fused23w(const int8_t *__restrict__ Vq,
+                                                               const float *__restrict__ sV,
+                                                               const int8_t *__restrict__ Uq,
+                                                               const float *__restrict__ sU,
+                                                               YT *__restrict__ y, Mats mt, Geo g) {
+    constexpr int N = M + 2, NT = N * N, MM = M * M, WPB = 4 * HT * HC, NTH = 64 * WPB;
+    constexpr int TPW = NT / WPB;            // taps per wave: 4 or 8
+    constexpr int NP = 256 * HT * HC;        // pairs per block
+    constexpr int CBW = NP / 16 / WPB;       // output column blocks per wave (4)
+    constexpr int RT = 16 * HT, RC = 16 * HC;  // tile rows of V, channel rows of U
     constexpr bool K64 = G % 64 == 0;
     constexpr int KSTEPS = K64 ? G / 64 : 1;
     constexpr int WLDS = NP * 64 / 4 / WPB;  // floats of the code rows per wave (1024)
-    static_assert(M == 6 && TPW * WPB == NT && TPW == 4, "F(6,3): four taps per wave");
-    static_assert(WLDS >= NP / WPB * WPB && WLDS >= 2 * TPW * 32, "per-wave LDS share");
+    constexpr int NSV = TPW * RT, NSC = TPW * (RT + RC);  // staged scales per wave
+    static_assert(M == 6 && TPW * WPB == NT && (TPW == 4 || TPW == 8), "F(6,3): 4 or 8 taps per wave");
+    static_assert(HT * HC >= 2 && HT <= 2 && HC <= 2, "2 x 2, 2 x 1 or 1 x 2 halves");
+    static_assert(WLDS >= NP && WLDS >= NSC && NSC % 64 == 0, "per-wave LDS share");
     __shared__ __attribute__((aligned(16))) uint8_t codes[NP * 64];
     __shared__ __attribute__((aligned(16))) _Float16 ktab[2][MM * 64];
     __shared__ float s_inv[NP], s_out[NP];
@@ -1467,17 +1471,17 @@ __global__ __launch_bounds__(1024, 1) void k_fused23w(const int8_t *__restrict__
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
-    const int nco = (g.Cout + 31) / 32;
-    const int ntb = (int)((g.T + 31) / 32);
+    const int nco = (g.Cout + RC - 1) / RC;
+    const int ntb = (int)((g.T + RT - 1) / RT);
     const int blk = xcd_block(blockIdx.x, gridDim.x);
     const int cob = g.co_major ? blk / ntb : blk % nco;
     const int tb = g.co_major ? blk % ntb : blk / nco;
-    const int t0 = tb * 32, co0 = cob * 32;
+    const int t0 = tb * RT, co0 = cob * RC;
     const int tap0 = wave * TPW;
     const size_t vplane = (size_t)g.T * g.Cin, uplane = (size_t)g.Cout * g.Cin;
     float *wlds = reinterpret_cast<float *>(codes) + wave * WLDS;
 
-    // ---- K = A^T (x) A^T, scaled, fp16 hi/lo (as in k_fused23)
+    // ---- K = A^T (x) A^T, scaled, fp16 hi/lo
     if (tid < M * N) at_lds[tid] = mt.At[tid];
     __syncthreads();
     fused_build_ktab<M, NTH>(at_lds, ktab, mt.kscale);
@@ -1491,59 +1495,79 @@ __global__ __launch_bounds__(1024, 1) void k_fused23w(const int8_t *__restrict__
     const auto rsU = make_rsrc(sU, (size_t)n2 * g.Cout * g.ng * 4);
     const bool kin = K64 || 8 * kq < G;
     const int koff = K64 ? 16 * kq : (kin ? 8 * kq : 0);
-    int voff[2], uoff[2];
+    int voff[HT], uoff[HC];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int tB = t0 + 16 * h + r, coA = co0 + 16 * h + r;
+    for (int h = 0; h < HT; ++h) {
+        const int tB = t0 + 16 * h + r;
         voff[h] = (tB < g.T ? tB : 0) * g.Cin + koff;
+    }
+#pragma unroll
+    for (int h = 0; h < HC; ++h) {
+        const int coA = co0 + 16 * h + r;
         uoff[h] = (coA < g.Cout ? coA : 0) * g.Cin + koff;
     }
-    float acc[TPW][2][2][4];
+    float acc[TPW][HC][HT][4];
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
 #pragma unroll
-        for (int hc = 0; hc < 2; ++hc)
+        for (int hc = 0; hc < HC; ++hc)
 #pragma unroll
-            for (int ht = 0; ht < 2; ++ht)
+            for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[j][hc][ht][i] = 0.0f;
 
     struct TapOps {
-        v4i a[2][K64 ? KSTEPS : 0], b[2][K64 ? KSTEPS : 0];
-        long a8[2], b8[2];
+        v4i a[HC][K64 ? KSTEPS : 0], b[HT][K64 ? KSTEPS : 0];
+        long a8[HC], b8[HT];
     };
     auto load_tap = [&](int j, int gi, TapOps &o) {
         const int tap = tap0 + j;
         const int vs = tap * (int)vplane + gi * G, us = tap * (int)uplane + gi * G;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < HC; ++h) {
             if constexpr (K64) {
 #pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) {
+                for (int ks = 0; ks < KSTEPS; ++ks)
                     o.a[h][ks] = __builtin_amdgcn_raw_buffer_load_b128(rU, uoff[h], us + ks * 64, 0);
-                    o.b[h][ks] = __builtin_amdgcn_raw_buffer_load_b128(rV, voff[h], vs + ks * 64, 0);
-                }
             } else {
                 const auto a2 = __builtin_amdgcn_raw_buffer_load_b64(rU, uoff[h], us, 0);
-                const auto b2 = __builtin_amdgcn_raw_buffer_load_b64(rV, voff[h], vs, 0);
                 o.a8[h] = ((long)(uint32_t)a2[1] << 32) | (uint32_t)a2[0];
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < HT; ++h) {
+            if constexpr (K64) {
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks)
+                    o.b[h][ks] = __builtin_amdgcn_raw_buffer_load_b128(rV, voff[h], vs + ks * 64, 0);
+            } else {
+                const auto b2 = __builtin_amdgcn_raw_buffer_load_b64(rV, voff[h], vs, 0);
                 o.b8[h] = ((long)(uint32_t)b2[1] << 32) | (uint32_t)b2[0];
             }
         }
     };
-    // group scales of this wave's taps, staged in its LDS share:
-    // wlds[(s * TPW + j) * 32 + row], s = 0: sV (row = tile), 1: sU (row = channel)
-    constexpr int SL = 2 * TPW * 32 / 64;
+    // group scales of this wave's taps, staged in its LDS share: sV of tap j
+    // at wlds[j * RT + row] (row = tile), then sU at wlds[NSV + j * RC + row]
+    constexpr int SL = NSC / 64;
     auto load_scales = [&](int gi, float (&sreg)[SL]) {
-        const int row = lane & 31;
-        const int tr = t0 + row < g.T ? t0 + row : 0, cr = co0 + row < g.Cout ? co0 + row : 0;
 #pragma unroll
         for (int k = 0; k < SL; ++k) {
             const int e = 64 * k + lane;
-            const int sw = e / (32 * TPW), j = (e / 32) % TPW;
+            const bool isv = e < NSV;
+            const int ev = isv ? e : e - NSV;
+            const int rows = isv ? RT : RC;
+            const int j = ev / rows, row = ev % rows;
             const int tap = tap0 + j;
-            const int off = sw == 0 ? ((tap * (int)g.T + tr) * g.ng + gi) * 4 : ((tap * g.Cout + cr) * g.ng + gi) * 4;
-            sreg[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sw == 0 ? rsV : rsU, off, 0, 0));
+            int off;
+            if (isv) {
+                const int tr = t0 + row < g.T ? t0 + row : 0;
+                off = ((tap * (int)g.T + tr) * g.ng + gi) * 4;
+            } else {
+                const int cr = co0 + row < g.Cout ? co0 + row : 0;
+                off = ((tap * g.Cout + cr) * g.ng + gi) * 4;
+            }
+            // which descriptor is uniform per load: NSV is a multiple of 64
+            sreg[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(64 * k < NSV ? rsV : rsU, off, 0, 0));
         }
     };
     auto put_scales = [&](const float (&sreg)[SL]) {
@@ -1552,9 +1576,9 @@ __global__ __launch_bounds__(1024, 1) void k_fused23w(const int8_t *__restrict__
     };
     auto use_tap = [&](int j, const TapOps &o) {
 #pragma unroll
-        for (int hc = 0; hc < 2; ++hc)
+        for (int hc = 0; hc < HC; ++hc)
 #pragma unroll
-            for (int ht = 0; ht < 2; ++ht) {
+            for (int ht = 0; ht < HT; ++ht) {
                 v4i P = v4i{0, 0, 0, 0};
                 if constexpr (K64) {
 #pragma unroll
@@ -1563,8 +1587,8 @@ __global__ __launch_bounds__(1024, 1) void k_fused23w(const int8_t *__restrict__
                 } else {
                     P = __builtin_amdgcn_mfma_i32_16x16x32_i8(kin ? o.a8[hc] : 0, kin ? o.b8[ht] : 0, P, 0, 0, 0);
                 }
-                const float sv = wlds[j * 32 + 16 * ht + r];
-                const float4 su = *(const float4 *)&wlds[(TPW + j) * 32 + 16 * hc + 4 * kq];
+                const float sv = wlds[j * RT + 16 * ht + r];
+                const float4 su = *(const float4 *)&wlds[NSV + j * RC + 16 * hc + 4 * kq];
                 const float sus[4] = {su.x, su.y, su.z, su.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[j][hc][ht][i] = __builtin_fmaf(sv * sus[i], (float)P[i], acc[j][hc][ht][i]);
@@ -1594,51 +1618,56 @@ __global__ __launch_bounds__(1024, 1) void k_fused23w(const int8_t *__restrict__
 
     // ---- Y absmax per pair: this wave's partial maxima in its LDS share
 #pragma unroll
-    for (int hc = 0; hc < 2; ++hc)
+    for (int hc = 0; hc < HC; ++hc)
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht)
+        for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float m = 0.0f;
 #pragma unroll
                 for (int j = 0; j < TPW; ++j) m = fmaxf(m, fabsf(acc[j][hc][ht][i]));
-                wlds[(16 * hc + 4 * kq + i) * 32 + 16 * ht + r] = m;
+                wlds[(16 * hc + 4 * kq + i) * RT + 16 * ht + r] = m;
             }
     __syncthreads();
-    {
+    for (int p = tid; p < NP; p += NTH) {
         const float *pm = reinterpret_cast<const float *>(codes);
-        float am = pm[tid];
+        float am = pm[p];
 #pragma unroll
-        for (int w = 1; w < WPB; ++w) am = fmaxf(am, pm[w * WLDS + tid]);
+        for (int w = 1; w < WPB; ++w) am = fmaxf(am, pm[w * WLDS + p]);
         float inv = 0.0f, sy = 0.0f;
         if (am != 0.0f) {
             inv = 127.0f / am;
             sy = am / 127.0f;
         }
-        s_inv[tid] = inv;
-        s_out[tid] = sy * mt.oscale;
+        s_inv[p] = inv;
+        s_out[p] = sy * mt.oscale;
     }
     __syncthreads();
-    // ---- codes of this wave's four taps, biased bytes, into the pair rows
+    // ---- codes of this wave's taps, biased bytes, into the pair rows
 #pragma unroll
-    for (int hc = 0; hc < 2; ++hc)
+    for (int hc = 0; hc < HC; ++hc)
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht)
+        for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int p = (16 * hc + 4 * kq + i) * 32 + 16 * ht + r;
+                const int p = (16 * hc + 4 * kq + i) * RT + 16 * ht + r;
                 const float inv = s_inv[p];
                 float yb[TPW];
 #pragma unroll
                 for (int j = 0; j < TPW; ++j) yb[j] = acc[j][hc][ht][i] * inv + kBiasedMagic;
-                *(uint32_t *)&codes[cswz(p, tap0 >> 3) + (tap0 & 7)] = pack4(yb[0], yb[1], yb[2], yb[3]);
+                if constexpr (TPW == 8) {
+                    const v2i w = {(int)pack4(yb[0], yb[1], yb[2], yb[3]), (int)pack4(yb[4], yb[5], yb[6], yb[7])};
+                    *(v2i *)&codes[cswz(p, tap0 >> 3)] = w;
+                } else {
+                    *(uint32_t *)&codes[cswz(p, tap0 >> 3) + (tap0 & 7)] = pack4(yb[0], yb[1], yb[2], yb[3]);
+                }
             }
     __syncthreads();
 
-    // ---- output transform: column block cb = wave + 16 c holds pairs
-    // 16 cb .. 16 cb + 15, i.e. channel co0 + cb / 2 and tiles
-    // t0 + 16 (cb % 2) + 0..15; cb % 2 == wave % 2 for all of a wave's blocks
-    fused_output<M, WPB, CBW, YT>(codes, ktab, s_out, wave, t0 + 16 * (wave & 1), co0 + (wave >> 1), WPB / 2,
+    // ---- output transform: column block cb = wave + WPB c holds pairs
+    // 16 cb .. 16 cb + 15, i.e. channel co0 + cb / HT and tiles
+    // t0 + 16 (cb % HT) + 0..15; cb % HT == wave % HT for all of a wave's blocks
+    fused_output<M, WPB, CBW, YT>(codes, ktab, s_out, wave, t0 + 16 * (wave % HT), co0 + wave / HT, WPB / HT,
                                   y, g);
 }
 
@@ -1820,11 +1849,21 @@ static void fused_m_g(const Geo &g, const Mats &mt, const int8_t *Vq, const floa
     const unsigned blocks = (unsigned)(((g.T + 15) / 16) * ((g.Cout + 15) / 16));
     if constexpr (M == 6 && G <= 64) {
         if (g.fused_wide) {
-            const unsigned wblocks = (unsigned)(((g.T + 31) / 32) * ((g.Cout + 31) / 32));
-            if (g.ng == 1)
-                hipLaunchKernelGGL((k_fused23w<M, G, false, YT>), dim3(wblocks), dim3(1024), 0, s, Vq, sV, Uq, sU, y, mt, g);
-            else
-                hipLaunchKernelGGL((k_fused23w<M, G, true, YT>), dim3(wblocks), dim3(1024), 0, s, Vq, sV, Uq, sU, y, mt, g);
+            // 1: 32 x 32 blocks, 2: 32 tiles x 16 channels, 3: 16 tiles x 32 channels
+            const int ht = g.fused_wide == 3 ? 1 : 2, hc = g.fused_wide == 2 ? 1 : 2;
+            const unsigned wblocks = (unsigned)(((g.T + 16 * ht - 1) / (16 * ht)) * ((g.Cout + 16 * hc - 1) / (16 * hc)));
+            const dim3 th(256 * ht * hc);
+#define WQ8_WIDE(HT_, HC_)                                                                                   \
+    do {                                                                                                     \
+        if (g.ng == 1)                                                                                       \
+            hipLaunchKernelGGL((k_fused23w<M, G, HT_, HC_, false, YT>), dim3(wblocks), th, 0, s, Vq, sV, Uq, sU, y, mt, g); \
+        else                                                                                                 \
+            hipLaunchKernelGGL((k_fused23w<M, G, HT_, HC_, true, YT>), dim3(wblocks), th, 0, s, Vq, sV, Uq, sU, y, mt, g);  \
+    } while (0)
+            if (ht == 2 && hc == 2) WQ8_WIDE(2, 2);
+            else if (ht == 2) WQ8_WIDE(2, 1);
+            else WQ8_WIDE(1, 2);
+#undef WQ8_WIDE
             return;
         }
     }

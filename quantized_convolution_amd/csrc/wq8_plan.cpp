@@ -494,17 +494,32 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
         const char *ov = getenv("WQ8_FUSED_WAVES");
         if (ov && (atoi(ov) == 4 || (m == 6 && (atoi(ov) == 8 || atoi(ov) == 16)))) w = atoi(ov);
         p->geo.fused_waves = w;
-        // 32 x 32 blocks of 16 waves (F(6,3), G <= 64): each tap's operands
-        // feed four MFMAs, halving the bytes a CU loads for the Hadamard
-        // products. They pay when the 16 x 16 blocks already stack three or
-        // more per CU and the wide blocks all fit at once (one per CU, by
-        // LDS): 18.5 -> 17.3 us on the 56 x 56 ResNet-18 layer; with fewer
-        // blocks they lose 5-90 %. WQ8_FUSED_WIDE = 0 or 1 overrides.
-        const int64_t nwide = ((g.T + 31) / 32) * (int64_t)((g.Cout + 31) / 32);
-        p->geo.fused_wide = m == 6 && d->group <= 64 && nblk >= 3 * 256 && nwide <= 256;
+        // Wide blocks (F(6,3), G <= 64) let each tap's operands feed two
+        // MFMAs: 16 tiles x 32 channels or 32 tiles x 16 channels (8 waves,
+        // 48 operand rows per block instead of 2 x 32 for two 16 x 16
+        // blocks). The busiest CU loads ceil(blocks / CUs) x (tile rows +
+        // channel rows) operand rows per tap and K byte; the shape with the
+        // fewest wins, ties to 16 x 32, then 32 x 16. Measured fused stage
+        // (16 x 16 -> 16 x 32): 56 x 56 ResNet-18 layer 18.5 -> 15.4 us, 28 x 28
+        // 22.8 -> 20.2 us, 14 x 14 39.1 -> 31.6 us; where the 16 x 16 blocks
+        // already give each CU one block (7 x 7, C = 512) the model keeps
+        // them (42 vs 61 us). 32 x 32 blocks of 16 waves (1) are slower than
+        // this model says on those layers and are only taken on request.
+        // WQ8_FUSED_WIDE = 0 (16 x 16), 1 (32 x 32), 2 (32 x 16) or 3
+        // (16 x 32) overrides.
+        auto busiest = [&](int64_t rt, int64_t rc) {
+            const int64_t nb = ((g.T + rt - 1) / rt) * ((g.Cout + rc - 1) / rc);
+            return ((nb + 255) / 256) * (rt + rc);
+        };
+        p->geo.fused_wide = 0;
+        if (m == 6 && d->group <= 64) {
+            const int64_t c0 = busiest(16, 16), c2 = busiest(32, 16), c3 = busiest(16, 32);
+            if (c3 <= c2 && c3 < c0) p->geo.fused_wide = 3;
+            else if (c2 < c0) p->geo.fused_wide = 2;
+        }
         const char *wide = getenv("WQ8_FUSED_WIDE");
-        if (wide && (atoi(wide) == 0 || atoi(wide) == 1))
-            p->geo.fused_wide = m == 6 && d->group <= 64 && atoi(wide) == 1;
+        if (wide && atoi(wide) >= 0 && atoi(wide) <= 3)
+            p->geo.fused_wide = m == 6 && d->group <= 64 ? atoi(wide) : 0;
     }
     // stage-1 window rows: WQ8_STAGE1_ROWS = full or half forces a form (for
     // tests); otherwise the launch picks half-row windows when the strips

@@ -338,9 +338,10 @@ def test_fused_block_shapes(dev, monkeypatch, waves, name, kw):
     ("c2_f6_n32_c64_56x56_g64", dict(N=2, H=30, W=26, Cin=64, Cout=40), None, torch.bfloat16),
 ])
 def test_fused_wide_blocks(dev, monkeypatch, name, kw, G, ydt):
-    """32 x 32 fused blocks (16 waves, each tap's operands feeding a 2 x 2 of
-    MFMAs): the oracle's result, and bit for bit the output of the 16 x 16
-    blocks, whose per-pair arithmetic they repeat."""
+    """Wide fused blocks (32 x 32, 32 tiles x 16 channels, 16 tiles x 32
+    channels; each tap's operands feed two or four MFMAs): the oracle's
+    result, and bit for bit the output of the 16 x 16 blocks, whose per-pair
+    arithmetic they repeat."""
     L = WL.small(WL.LAYERS[name], **kw)
     if G is not None:
         L = L.replace(G=G, name=L.name + f"_g{G}")
@@ -348,13 +349,14 @@ def test_fused_wide_blocks(dev, monkeypatch, name, kw, G, ydt):
     d = WL.make(L)
     x, w = to_dev(d["x"], dev), to_dev(d["w"], dev)
     outs = {}
-    for wide in ("0", "1"):
+    for wide in ("0", "1", "2", "3"):
         monkeypatch.setenv("WQ8_FUSED_WIDE", wide)
         plan = make_plan(L, d, ydt=ydt, algo="fused")
         Uq, sU = q.wq8_weights_prepare(plan, w)
         outs[wide] = q.wq8_conv_forward(plan, x, Uq, sU)
         torch.cuda.synchronize()
-    assert torch.equal(outs["0"], outs["1"]), "wide and 16 x 16 fused blocks differ"
+    for wide in ("1", "2", "3"):
+        assert torch.equal(outs["0"], outs[wide]), f"wide blocks ({wide}) and 16 x 16 blocks differ"
     if ydt is None:
         ref = oracle.forward(L.m, d["x"], d["w"], L.pad, L.G, points=list(d["points"]), s_b=d["s_b"],
                              s_g=d["s_g"])
