@@ -1034,8 +1034,8 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
 // padded to BS, so a lane's four rows are adjacent pixels of one output row.
 //
 // LDS stays below 40 KB and registers below 128 so that four blocks share a
-// CU: on the ResNet-18 layer all 800 blocks then run in a single wave of
-// residency instead of 768 plus a tail of 32.
+// CU: with 800 blocks (16 x 16 blocks on the ResNet-18 layer) they then run
+// in a single wave of residency instead of 768 plus a tail of 32.
 constexpr float kBiasedMagic = 12583040.0f;  // 1.5 * 2^23 + 128 (even)
 
 // Code rows: 64 bytes per pair; 8-byte chunk c of pair p at c ^ ((p >> 2) & 7).
