@@ -326,6 +326,7 @@ def test_fused_block_shapes(dev, monkeypatch, waves, name, kw):
     assert_out(y.cpu().numpy(), ref, f"fused forward, {waves} waves")
 
 
+@pytest.mark.parametrize("pad", [None, 0, 2])
 @pytest.mark.parametrize("name,kw,G,ydt", [
     # tiles and channels not multiples of 32
     ("c2_f6_n32_c64_56x56_g64", dict(N=2, H=30, W=26, Cin=64, Cout=40), None, None),
@@ -336,8 +337,10 @@ def test_fused_block_shapes(dev, monkeypatch, waves, name, kw):
     ("c3c_f6_n32_c512_7x7_g64", dict(N=3, H=7, W=7, Cin=192, Cout=72), None, None),
     # bf16 output
     ("c2_f6_n32_c64_56x56_g64", dict(N=2, H=30, W=26, Cin=64, Cout=40), None, torch.bfloat16),
+    # two tiles in all (blocks almost all padding), one output channel past a block
+    ("c2_f6_n32_c64_56x56_g64", dict(N=1, H=5, W=9, Cin=64, Cout=33), None, None),
 ])
-def test_fused_wide_blocks(dev, monkeypatch, name, kw, G, ydt):
+def test_fused_wide_blocks(dev, monkeypatch, name, kw, G, ydt, pad):
     """Wide fused blocks (32 x 32, 32 tiles x 16 channels, 16 tiles x 32
     channels; each tap's operands feed two or four MFMAs): the oracle's
     result, and bit for bit the output of the 16 x 16 blocks, whose per-pair
@@ -345,6 +348,8 @@ def test_fused_wide_blocks(dev, monkeypatch, name, kw, G, ydt):
     L = WL.small(WL.LAYERS[name], **kw)
     if G is not None:
         L = L.replace(G=G, name=L.name + f"_g{G}")
+    if pad is not None:
+        L = L.replace(pad=pad, name=L.name + f"_pad{pad}")
     print(f"\n[case] fused wide {L.name} C={L.Cin}->{L.Cout} {L.H}x{L.W} G={L.G} y={ydt}", flush=True)
     d = WL.make(L)
     x, w = to_dev(d["x"], dev), to_dev(d["w"], dev)
