@@ -134,7 +134,17 @@ typedef struct {
 
 /* Validates the descriptor and builds the scaled transforms on the host (exact
  * rational arithmetic, each entry rounded once to fp32, ties to even). No
- * device work. The caller owns *out and frees it with wq8_plan_destroy. */
+ * device work. The caller owns *out and frees it with wq8_plan_destroy.
+ *
+ * Kernel shapes are chosen here too; three environment variables, read at
+ * creation, force one (for tests and measurement; results are the same bit
+ * for bit, except where the fused schedule's output transform applies):
+ *   WQ8_STAGE1_ROWS = full | half   input-transform LDS window rows;
+ *   WQ8_FUSED_WAVES = 4 | 8 | 16     waves of a 16 x 16 fused block;
+ *   WQ8_FUSED_WIDE  = 0 | 1 | 2 | 3  fused blocks of 16 x 16, 32 x 32,
+ *                                    32 tiles x 16 channels or 16 x 32
+ *                                    (F(6,3), G <= 64 only).
+ * Other values are ignored. */
 wq8_status wq8_plan_create(const wq8_desc *desc, wq8_plan **out);
 void wq8_plan_destroy(wq8_plan *plan);
 
