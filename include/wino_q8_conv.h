@@ -137,8 +137,10 @@ typedef struct {
  * device work. The caller owns *out and frees it with wq8_plan_destroy.
  *
  * Kernel shapes are chosen here too; three environment variables, read at
- * creation, force one (for tests and measurement; results are the same bit
- * for bit, except where the fused schedule's output transform applies):
+ * creation, force one (for tests and measurement). Every shape performs the
+ * same operations per output in the same order, so results do not depend on
+ * the choice (the tests compare the stage-1 windows and the wide and 16 x 16
+ * fused blocks bit for bit):
  *   WQ8_STAGE1_ROWS = full | half   input-transform LDS window rows;
  *   WQ8_FUSED_WAVES = 4 | 8 | 16     waves of a 16 x 16 fused block;
  *   WQ8_FUSED_WIDE  = 0 | 1 | 2 | 3  fused blocks of 16 x 16, 32 x 32,
