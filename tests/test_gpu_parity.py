@@ -326,6 +326,28 @@ def test_fused_block_shapes(dev, monkeypatch, waves, name, kw):
     assert_out(y.cpu().numpy(), ref, f"fused forward, {waves} waves")
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("c2_f6_n32_c64_56x56_g64", dict(N=2, H=30, W=26, Cin=64, Cout=40)),
+    ("c5_f6_n8_c640_32x32_g32", dict(N=1, H=13, W=17, Cin=96, Cout=20)),
+])
+def test_fused_wave_counts_agree(dev, monkeypatch, name, kw):
+    """16 x 16 fused blocks of 4, 8 and 16 waves split the same per-pair work
+    differently: their outputs agree bit for bit."""
+    L = WL.small(WL.LAYERS[name], **kw)
+    print(f"\n[case] fused wave counts {L.name}", flush=True)
+    d = WL.make(L)
+    x, w = to_dev(d["x"], dev), to_dev(d["w"], dev)
+    monkeypatch.setenv("WQ8_FUSED_WIDE", "0")
+    outs = {}
+    for waves in ("4", "8", "16"):
+        monkeypatch.setenv("WQ8_FUSED_WAVES", waves)
+        plan = make_plan(L, d, algo="fused")
+        Uq, sU = q.wq8_weights_prepare(plan, w)
+        outs[waves] = q.wq8_conv_forward(plan, x, Uq, sU)
+        torch.cuda.synchronize()
+    assert torch.equal(outs["4"], outs["8"]) and torch.equal(outs["4"], outs["16"])
+
+
 @pytest.mark.parametrize("pad", [None, 0, 2])
 @pytest.mark.parametrize("name,kw,G,ydt", [
     # tiles and channels not multiples of 32
