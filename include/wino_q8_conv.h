@@ -130,23 +130,23 @@ typedef struct {
     wq8_algo algo;         /* stage 2 + 3 schedule for wq8_conv_forward */
     wq8_ygroup y_group;    /* Y scale granularity (TILE unless stated) */
     wq8_inq in_quant;      /* input-stage reading (FP32 unless stated) */
+    /* Kernel shapes, for tests and tuning; 0 lets the library choose (by block
+     * count against the device's compute units, at launch). Every shape
+     * performs the same operations per output in the same order, so results
+     * do not depend on the choice. A value out of range is
+     * WQ8_ERR_INVALID_ARG; a shape not built for the layer is
+     * WQ8_ERR_UNSUPPORTED. */
+    int stage1_rows;       /* input-transform LDS window: 1 all n input rows,
+                              2 half of them at a time (FP32 input stage) */
+    int fused_waves;       /* waves of a 16 x 16 fused block: 4; 8 or 16 for F(6,3) */
+    int fused_block;       /* fused block: 1 16 tiles x 16 output channels;
+                              F(6,3) with G <= 64 also 2 32 x 32, 3 32 tiles x
+                              16 channels, 4 16 tiles x 32 channels */
 } wq8_desc;
 
 /* Validates the descriptor and builds the scaled transforms on the host (exact
  * rational arithmetic, each entry rounded once to fp32, ties to even). No
- * device work. The caller owns *out and frees it with wq8_plan_destroy.
- *
- * Kernel shapes are chosen here too; three environment variables, read at
- * creation, force one (for tests and measurement). Every shape performs the
- * same operations per output in the same order, so results do not depend on
- * the choice (the tests compare the stage-1 windows and the wide and 16 x 16
- * fused blocks bit for bit):
- *   WQ8_STAGE1_ROWS = full | half   input-transform LDS window rows;
- *   WQ8_FUSED_WAVES = 4 | 8 | 16     waves of a 16 x 16 fused block;
- *   WQ8_FUSED_WIDE  = 0 | 1 | 2 | 3  fused blocks of 16 x 16, 32 x 32,
- *                                    32 tiles x 16 channels or 16 x 32
- *                                    (F(6,3), G <= 64 only).
- * Other values are ignored. */
+ * device work. The caller owns *out and frees it with wq8_plan_destroy. */
 wq8_status wq8_plan_create(const wq8_desc *desc, wq8_plan **out);
 void wq8_plan_destroy(wq8_plan *plan);
 

@@ -36,7 +36,8 @@ class wq8_desc(C.Structure):
                 ("group", C.c_int), ("N", C.c_int), ("Cin", C.c_int), ("Cout", C.c_int),
                 ("H", C.c_int), ("W", C.c_int), ("pad", C.c_int),
                 ("x_dtype", C.c_int), ("y_dtype", C.c_int), ("algo", C.c_int), ("y_group", C.c_int),
-                ("in_quant", C.c_int)]
+                ("in_quant", C.c_int), ("stage1_rows", C.c_int), ("fused_waves", C.c_int),
+                ("fused_block", C.c_int)]
 
 
 EXPORTS = ("wq8_plan_create", "wq8_plan_destroy", "wq8_plan_query", "wq8_plan_matrices",
@@ -98,17 +99,50 @@ def _check(st: int):
 def _ptr(t):
     if t is None:
         return None
-    if not isinstance(t, torch.Tensor):
-        raise TypeError("device buffers must be torch tensors")
-    if not t.is_contiguous():
-        raise ValueError("device buffers must be contiguous")
     return C.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return C.c_void_p(stream.cuda_stream)
+class _Bufs:
+    """Checks every buffer of one call before anything reaches the library:
+    a torch tensor of the expected dtype and shape (or, for a workspace, at
+    least the expected bytes), contiguous, and (checked last, for all of them
+    together) on a GPU, all on one device. The kernels size their accesses
+    from the plan, so a buffer that fails any of these would be read or
+    written out of bounds; ValueError instead."""
+
+    def __init__(self):
+        self.device = None
+        self.bufs = []
+
+    def __call__(self, t, name, dtype, shape=None, min_bytes=None):
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+            raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {min_bytes}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        self.bufs.append((name, t))
+        return t
+
+    def call(self, fn, *args, stream=None):
+        """Check the devices, then run the C call with the buffers' device
+        current, on `stream` or that device's current stream."""
+        for name, t in self.bufs:
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} must be on a GPU, got {t.device}")
+            if self.device is None:
+                self.device = t.device
+            elif t.device != self.device:
+                raise ValueError(f"{name} is on {t.device}, other buffers on {self.device}")
+        with torch.cuda.device(self.device):
+            st = torch.cuda.current_stream(self.device) if stream is None else stream
+            _check(fn(*args, C.c_void_p(st.cuda_stream)))
 
 
 class Plan:
@@ -116,7 +150,11 @@ class Plan:
 
     def __init__(self, m, N, Cin, Cout, H, W, pad=1, group=64, points=None, s_B=None, s_G=None,
                  x_dtype=torch.float32, y_dtype=None, algo="auto", y_group="tile",
-                 in_quant="fp32"):
+                 in_quant="fp32", stage1_rows=0, fused_waves=0, fused_block=0):
+        """Kernel shapes (0 = the library chooses; results never depend on
+        them): stage1_rows 1 all / 2 half the input rows in the LDS window;
+        fused_waves 4, 8 or 16; fused_block 1 16x16, 2 32x32, 3 32 tiles x 16
+        channels, 4 16 x 32."""
         lib = load()
         n = m + 2
         self.m, self.n, self.N, self.Cin, self.Cout, self.H, self.W = m, n, N, Cin, Cout, H, W
@@ -139,7 +177,7 @@ class Plan:
         d = wq8_desc(m, arr(points, C.c_double, np.float64), arr(s_B, C.c_float, np.float32),
                      arr(s_G, C.c_float, np.float32), group, N, Cin, Cout, H, W, pad,
                      _DT[self.x_dtype], _DT[self.y_dtype], ALGOS[algo], YGROUPS[y_group],
-                     IN_QUANTS[in_quant])
+                     IN_QUANTS[in_quant], int(stage1_rows), int(fused_waves), int(fused_block))
         h = C.c_void_p()
         self._h = None
         _check(wq8_plan_create(d, h))
@@ -167,6 +205,35 @@ class Plan:
 
     def direct_ops(self) -> int:
         return 2 * self.N * self.Cin * self.Cout * self.Ho * self.Wo * 9
+
+    # ---- buffer shapes the kernels assume ----
+    @property
+    def x_shape(self):
+        return (self.N, self.Cin, self.H, self.W)
+
+    @property
+    def y_shape(self):
+        return (self.N, self.Cout, self.Ho, self.Wo)
+
+    @property
+    def uq_shape(self):
+        return (self.n * self.n, self.Cout, self.Cin)
+
+    @property
+    def su_shape(self):
+        return (self.n * self.n, self.Cout, self.ng)
+
+    @property
+    def vq_shape(self):
+        return (self.n * self.n, self.T, self.Cin)
+
+    @property
+    def sv_shape(self):
+        return (self.n * self.n, self.T, self.ng)
+
+    @property
+    def m_shape(self):
+        return (self.n * self.n, self.T, self.Cout)
 
     # ---- buffers (torch is the allocator) ----
     def empty_weights(self, device="cuda"):
@@ -206,73 +273,111 @@ def wq8_plan_bt_codes(plan: Plan):
 
 
 def wq8_weights_prepare(plan: Plan, w, Uq=None, sU=None, stream=None):
-    if w.dtype != torch.float32 or tuple(w.shape) != (plan.Cout, plan.Cin, 3, 3):
-        raise ValueError("w must be float32 [Cout][Cin][3][3]")
+    b = _Bufs()
+    b(w, "w", torch.float32, (plan.Cout, plan.Cin, 3, 3))
     if Uq is None:
         Uq, sU = plan.empty_weights(w.device)
-    _check(load().wq8_weights_prepare(plan.handle, _ptr(w), _ptr(Uq), _ptr(sU), _stream(stream)))
+    b(Uq, "Uq", torch.int8, plan.uq_shape)
+    b(sU, "sU", torch.float32, plan.su_shape)
+    b.call(load().wq8_weights_prepare, plan.handle, _ptr(w), _ptr(Uq), _ptr(sU), stream=stream)
     return Uq, sU
 
 
-def _check_x(plan, x):
-    if x.dtype != plan.x_dtype or tuple(x.shape) != (plan.N, plan.Cin, plan.H, plan.W):
-        raise ValueError(f"x must be {plan.x_dtype} {(plan.N, plan.Cin, plan.H, plan.W)}")
+def _check_x(plan, b, x):
+    b(x, "x", plan.x_dtype, plan.x_shape)
+
+
+def _check_weights(plan, b, Uq, sU):
+    b(Uq, "Uq", torch.int8, plan.uq_shape)
+    b(sU, "sU", torch.float32, plan.su_shape)
+
+
+def _check_codes(plan, b, Vq, sV):
+    b(Vq, "Vq", torch.int8, plan.vq_shape)
+    b(sV, "sV", torch.float32, plan.sv_shape)
 
 
 def wq8_conv_forward(plan: Plan, x, Uq, sU, y=None, workspace=None, stream=None):
-    _check_x(plan, x)
+    b = _Bufs()
+    _check_x(plan, b, x)
+    _check_weights(plan, b, Uq, sU)
     if y is None:
         y = plan.empty_output(x.device)
     if workspace is None:
         workspace = plan.empty_workspace(x.device)
+    b(y, "y", plan.y_dtype, plan.y_shape)
+    b(workspace, "workspace", None, min_bytes=plan.workspace_bytes)
+    if y.data_ptr() == x.data_ptr():
+        raise ValueError("x and y must not overlap")
     nbytes = workspace.numel() * workspace.element_size()
-    _check(load().wq8_conv_forward(plan.handle, _ptr(x), _ptr(Uq), _ptr(sU), _ptr(y),
-                                   _ptr(workspace), nbytes, _stream(stream)))
+    b.call(load().wq8_conv_forward, plan.handle, _ptr(x), _ptr(Uq), _ptr(sU), _ptr(y),
+           _ptr(workspace), C.c_size_t(nbytes), stream=stream)
     return y
 
 
 def wq8_stage1(plan: Plan, x, Vq=None, sV=None, stream=None):
-    _check_x(plan, x)
-    n2 = plan.n * plan.n
+    b = _Bufs()
+    _check_x(plan, b, x)
     if Vq is None:
-        Vq = torch.empty((n2, plan.T, plan.Cin), dtype=torch.int8, device=x.device)
-        sV = torch.empty((n2, plan.T, plan.ng), dtype=torch.float32, device=x.device)
-    _check(load().wq8_stage1(plan.handle, _ptr(x), _ptr(Vq), _ptr(sV), _stream(stream)))
+        Vq = torch.empty(plan.vq_shape, dtype=torch.int8, device=x.device)
+        sV = torch.empty(plan.sv_shape, dtype=torch.float32, device=x.device)
+    _check_codes(plan, b, Vq, sV)
+    b.call(load().wq8_stage1, plan.handle, _ptr(x), _ptr(Vq), _ptr(sV), stream=stream)
     return Vq, sV
 
 
 def wq8_stage2(plan: Plan, Vq, sV, Uq, sU, M=None, stream=None):
+    b = _Bufs()
+    _check_codes(plan, b, Vq, sV)
+    _check_weights(plan, b, Uq, sU)
     if M is None:
-        M = torch.empty((plan.n * plan.n, plan.T, plan.Cout), dtype=torch.float32, device=Vq.device)
-    _check(load().wq8_stage2(plan.handle, _ptr(Vq), _ptr(sV), _ptr(Uq), _ptr(sU), _ptr(M),
-                             _stream(stream)))
+        M = torch.empty(plan.m_shape, dtype=torch.float32, device=Vq.device)
+    b(M, "M", torch.float32, plan.m_shape)
+    b.call(load().wq8_stage2, plan.handle, _ptr(Vq), _ptr(sV), _ptr(Uq), _ptr(sU), _ptr(M),
+           stream=stream)
     return M
 
 
 def wq8_stage2_i32(plan: Plan, Vq, Uq, P=None, stream=None):
+    b = _Bufs()
+    b(Vq, "Vq", torch.int8, plan.vq_shape)
+    b(Uq, "Uq", torch.int8, plan.uq_shape)
+    pshape = (plan.n * plan.n, plan.ng, plan.T, plan.Cout)
     if P is None:
-        P = torch.empty((plan.n * plan.n, plan.ng, plan.T, plan.Cout), dtype=torch.int32,
-                        device=Vq.device)
-    _check(load().wq8_stage2_i32(plan.handle, _ptr(Vq), _ptr(Uq), _ptr(P), _stream(stream)))
+        P = torch.empty(pshape, dtype=torch.int32, device=Vq.device)
+    b(P, "P", torch.int32, pshape)
+    b.call(load().wq8_stage2_i32, plan.handle, _ptr(Vq), _ptr(Uq), _ptr(P), stream=stream)
     return P
 
 
 def wq8_stage3(plan: Plan, M, y=None, Yq=None, sY=None, want_codes=False, stream=None):
+    b = _Bufs()
+    b(M, "M", torch.float32, plan.m_shape)
     if y is None:
         y = plan.empty_output(M.device)
+    b(y, "y", plan.y_dtype, plan.y_shape)
+    sshape = (plan.T, plan.Cout, plan.n) if plan.y_group == "row" else (plan.T, plan.Cout)
+    yqshape = (plan.T, plan.Cout, plan.n * plan.n)
     if want_codes and Yq is None:
-        Yq = torch.empty((plan.T, plan.Cout, plan.n * plan.n), dtype=torch.int8, device=M.device)
-        sshape = (plan.T, plan.Cout, plan.n) if plan.y_group == "row" else (plan.T, plan.Cout)
+        Yq = torch.empty(yqshape, dtype=torch.int8, device=M.device)
         sY = torch.empty(sshape, dtype=torch.float32, device=M.device)
-    _check(load().wq8_stage3(plan.handle, _ptr(M), _ptr(y), _ptr(Yq), _ptr(sY), _stream(stream)))
+    if Yq is not None:
+        b(Yq, "Yq", torch.int8, yqshape)
+    if sY is not None:
+        b(sY, "sY", torch.float32, sshape)
+    b.call(load().wq8_stage3, plan.handle, _ptr(M), _ptr(y), _ptr(Yq), _ptr(sY), stream=stream)
     return (y, Yq, sY) if want_codes else y
 
 
 def wq8_stage23(plan: Plan, Vq, sV, Uq, sU, y=None, stream=None):
+    b = _Bufs()
+    _check_codes(plan, b, Vq, sV)
+    _check_weights(plan, b, Uq, sU)
     if y is None:
         y = plan.empty_output(Vq.device)
-    _check(load().wq8_stage23(plan.handle, _ptr(Vq), _ptr(sV), _ptr(Uq), _ptr(sU), _ptr(y),
-                              _stream(stream)))
+    b(y, "y", plan.y_dtype, plan.y_shape)
+    b.call(load().wq8_stage23, plan.handle, _ptr(Vq), _ptr(sV), _ptr(Uq), _ptr(sU), _ptr(y),
+           stream=stream)
     return y
 
 
@@ -282,40 +387,67 @@ def tiles(m, N, H, W, pad):
 
 
 # ---- group-wise W8A8 direct convolution (the non-Winograd baseline)
+def _direct_shapes(plan):
+    return ((9, plan.Cout, plan.Cin), (9, plan.Cout, plan.ng),
+            (plan.N, plan.H, plan.W, plan.Cin), (plan.N, plan.H, plan.W, plan.ng))
+
+
 def wq8_direct_weights_prepare(plan: Plan, w, Wq=None, sW=None, stream=None):
-    if w.dtype != torch.float32 or tuple(w.shape) != (plan.Cout, plan.Cin, 3, 3):
-        raise ValueError("w must be float32 [Cout][Cin][3][3]")
+    wqs, sws, _, _ = _direct_shapes(plan)
+    b = _Bufs()
+    b(w, "w", torch.float32, (plan.Cout, plan.Cin, 3, 3))
     if Wq is None:
-        Wq = torch.empty((9, plan.Cout, plan.Cin), dtype=torch.int8, device=w.device)
-        sW = torch.empty((9, plan.Cout, plan.ng), dtype=torch.float32, device=w.device)
-    _check(load().wq8_direct_weights_prepare(plan.handle, _ptr(w), _ptr(Wq), _ptr(sW), _stream(stream)))
+        Wq = torch.empty(wqs, dtype=torch.int8, device=w.device)
+        sW = torch.empty(sws, dtype=torch.float32, device=w.device)
+    b(Wq, "Wq", torch.int8, wqs)
+    b(sW, "sW", torch.float32, sws)
+    b.call(load().wq8_direct_weights_prepare, plan.handle, _ptr(w), _ptr(Wq), _ptr(sW), stream=stream)
     return Wq, sW
 
 
 def wq8_direct_quantize_x(plan: Plan, x, Xq=None, sX=None, stream=None):
-    _check_x(plan, x)
+    _, _, xqs, sxs = _direct_shapes(plan)
+    b = _Bufs()
+    _check_x(plan, b, x)
     if Xq is None:
-        Xq = torch.empty((plan.N, plan.H, plan.W, plan.Cin), dtype=torch.int8, device=x.device)
-        sX = torch.empty((plan.N, plan.H, plan.W, plan.ng), dtype=torch.float32, device=x.device)
-    _check(load().wq8_direct_quantize_x(plan.handle, _ptr(x), _ptr(Xq), _ptr(sX), _stream(stream)))
+        Xq = torch.empty(xqs, dtype=torch.int8, device=x.device)
+        sX = torch.empty(sxs, dtype=torch.float32, device=x.device)
+    b(Xq, "Xq", torch.int8, xqs)
+    b(sX, "sX", torch.float32, sxs)
+    b.call(load().wq8_direct_quantize_x, plan.handle, _ptr(x), _ptr(Xq), _ptr(sX), stream=stream)
     return Xq, sX
 
 
 def wq8_direct_conv(plan: Plan, Xq, sX, Wq, sW, y=None, stream=None):
+    wqs, sws, xqs, sxs = _direct_shapes(plan)
+    b = _Bufs()
+    b(Xq, "Xq", torch.int8, xqs)
+    b(sX, "sX", torch.float32, sxs)
+    b(Wq, "Wq", torch.int8, wqs)
+    b(sW, "sW", torch.float32, sws)
     if y is None:
         y = plan.empty_output(Xq.device)
-    _check(load().wq8_direct_conv(plan.handle, _ptr(Xq), _ptr(sX), _ptr(Wq), _ptr(sW), _ptr(y),
-                                  _stream(stream)))
+    b(y, "y", plan.y_dtype, plan.y_shape)
+    b.call(load().wq8_direct_conv, plan.handle, _ptr(Xq), _ptr(sX), _ptr(Wq), _ptr(sW), _ptr(y),
+           stream=stream)
     return y
 
 
 def wq8_direct_forward(plan: Plan, x, Wq, sW, y=None, workspace=None, stream=None):
-    _check_x(plan, x)
+    wqs, sws, _, _ = _direct_shapes(plan)
+    b = _Bufs()
+    _check_x(plan, b, x)
+    b(Wq, "Wq", torch.int8, wqs)
+    b(sW, "sW", torch.float32, sws)
     if y is None:
         y = plan.empty_output(x.device)
     if workspace is None:
         workspace = torch.empty(plan.direct_workspace_bytes, dtype=torch.uint8, device=x.device)
+    b(y, "y", plan.y_dtype, plan.y_shape)
+    b(workspace, "workspace", None, min_bytes=plan.direct_workspace_bytes)
+    if y.data_ptr() == x.data_ptr():
+        raise ValueError("x and y must not overlap")
     nbytes = workspace.numel() * workspace.element_size()
-    _check(load().wq8_direct_forward(plan.handle, _ptr(x), _ptr(Wq), _ptr(sW), _ptr(y),
-                                     _ptr(workspace), nbytes, _stream(stream)))
+    b.call(load().wq8_direct_forward, plan.handle, _ptr(x), _ptr(Wq), _ptr(sW), _ptr(y),
+           _ptr(workspace), C.c_size_t(nbytes), stream=stream)
     return y

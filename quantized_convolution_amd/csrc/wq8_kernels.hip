@@ -1843,14 +1843,53 @@ static void stage3_m(const Geo &g, const Mats &mt, const float *Mi, YT *y, int8_
     else hipLaunchKernelGGL((k_stage3<M, false, YT>), grid, dim3(256), 0, s, Mi, y, Yq, sY, mt, g);
 }
 
+// Fused block shape for a layer: waves per 16 x 16 block and the wide form
+// (0 16 x 16; 1 32 x 32, 2 32 tiles x 16 channels, 3 16 tiles x 32 channels).
+// The plan's values win where it forced one.
+//   Waves: with at least three 16 x 16 blocks per CU, 4-wave blocks keep every
+//   block resident at once (up to five fit a CU); with fewer blocks, 8-wave
+//   blocks (F(6,3): 8 taps per wave, all loaded at once) put more loads in
+//   flight per block: 4-10 % faster on the deeper layers, 2 % slower on the
+//   56 x 56 ResNet-18 layer. 16 waves were never faster.
+//   Wide blocks (F(6,3), G <= 64) let each tap's operands feed two MFMAs
+//   (48 operand rows per block instead of 2 x 32 for two 16 x 16 blocks).
+//   The busiest CU loads ceil(blocks / CUs) x (tile rows + channel rows)
+//   operand rows per tap and K byte; the shape with the fewest wins, ties to
+//   16 x 32, then 32 x 16. Measured fused stage (16 x 16 -> 16 x 32): 56 x 56
+//   ResNet-18 layer 18.5 -> 15.4 us, 28 x 28 22.8 -> 20.2 us, 14 x 14
+//   39.1 -> 31.6 us; where 16 x 16 blocks already give each CU one block
+//   (7 x 7, C = 512) the model keeps them (42 vs 61 us). 32 x 32 blocks of
+//   16 waves run slower than the model says on those layers and are only
+//   taken when forced.
+static void fused_shape(const Geo &g, int cus, int &waves, int &wide) {
+    const int64_t nblk = ((g.T + 15) / 16) * (int64_t)((g.Cout + 15) / 16);
+    waves = g.fused_waves ? g.fused_waves : g.m == 6 && nblk < 3 * (int64_t)cus ? 8 : 4;
+    if (g.fused_wide >= 0) {
+        wide = g.fused_wide;
+        return;
+    }
+    wide = 0;
+    if (g.m == 6 && g.G <= 64) {
+        auto busiest = [&](int64_t rt, int64_t rc) {
+            const int64_t nb = ((g.T + rt - 1) / rt) * ((g.Cout + rc - 1) / rc);
+            return ((nb + cus - 1) / cus) * (rt + rc);
+        };
+        const int64_t c0 = busiest(16, 16), c2 = busiest(32, 16), c3 = busiest(16, 32);
+        if (c3 <= c2 && c3 < c0) wide = 3;
+        else if (c2 < c0) wide = 2;
+    }
+}
+
 template <int M, int G, typename YT>
 static void fused_m_g(const Geo &g, const Mats &mt, const int8_t *Vq, const float *sV,
                       const int8_t *Uq, const float *sU, YT *y, hipStream_t s) {
     const unsigned blocks = (unsigned)(((g.T + 15) / 16) * ((g.Cout + 15) / 16));
+    int waves, wide;
+    fused_shape(g, device_cus(), waves, wide);
     if constexpr (M == 6 && G <= 64) {
-        if (g.fused_wide) {
+        if (wide) {
             // 1: 32 x 32 blocks, 2: 32 tiles x 16 channels, 3: 16 tiles x 32 channels
-            const int ht = g.fused_wide == 3 ? 1 : 2, hc = g.fused_wide == 2 ? 1 : 2;
+            const int ht = wide == 3 ? 1 : 2, hc = wide == 2 ? 1 : 2;
             const unsigned wblocks = (unsigned)(((g.T + 16 * ht - 1) / (16 * ht)) * ((g.Cout + 16 * hc - 1) / (16 * hc)));
             const dim3 th(256 * ht * hc);
 #define WQ8_WIDE(HT_, HC_)                                                                                   \
@@ -1870,14 +1909,14 @@ static void fused_m_g(const Geo &g, const Mats &mt, const int8_t *Vq, const floa
     // waves per block as the plan chose (8 or 16 split the taps further; F(4,3)
     // has 36 taps and always uses 4)
     if constexpr (M == 6) {
-        if (g.fused_waves == 8) {
+        if (waves == 8) {
             if (g.ng == 1)
                 hipLaunchKernelGGL((k_fused23<M, G, 8, false, YT>), dim3(blocks), dim3(512), 0, s, Vq, sV, Uq, sU, y, mt, g);
             else
                 hipLaunchKernelGGL((k_fused23<M, G, 8, true, YT>), dim3(blocks), dim3(512), 0, s, Vq, sV, Uq, sU, y, mt, g);
             return;
         }
-        if (g.fused_waves == 16) {
+        if (waves == 16) {
             if (g.ng == 1)
                 hipLaunchKernelGGL((k_fused23<M, G, 16, false, YT>), dim3(blocks), dim3(1024), 0, s, Vq, sV, Uq, sU, y, mt, g);
             else

@@ -481,53 +481,26 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
     // every tile block all weights of its channels: keep the larger operand
     // split across the XCDs' L2s
     p->geo.co_major = p->u_code_bytes > (size_t)(n2 * g.T * g.Cin);
-    // fused kernel, waves per block (the taps are split between them). With
-    // at least three blocks per CU of MI355X (256 CUs), 4-wave blocks keep
-    // every block resident at once (up to five fit a CU); with fewer blocks,
-    // 8-wave blocks (F(6,3) only: 8 taps per wave, all loaded at once) put
-    // more loads in flight per block: 4-10 % faster on the deeper layers,
-    // 2 % slower on the 56 x 56 ResNet-18 layer. WQ8_FUSED_WAVES = 4, 8 or 16
-    // overrides the choice (16 is kept for comparison; it was never faster).
-    {
-        const int64_t nblk = ((g.T + 15) / 16) * (int64_t)((g.Cout + 15) / 16);
-        int w = m == 6 && nblk < 3 * 256 ? 8 : 4;
-        const char *ov = getenv("WQ8_FUSED_WAVES");
-        if (ov && (atoi(ov) == 4 || (m == 6 && (atoi(ov) == 8 || atoi(ov) == 16)))) w = atoi(ov);
-        p->geo.fused_waves = w;
-        // Wide blocks (F(6,3), G <= 64) let each tap's operands feed two
-        // MFMAs: 16 tiles x 32 channels or 32 tiles x 16 channels (8 waves,
-        // 48 operand rows per block instead of 2 x 32 for two 16 x 16
-        // blocks). The busiest CU loads ceil(blocks / CUs) x (tile rows +
-        // channel rows) operand rows per tap and K byte; the shape with the
-        // fewest wins, ties to 16 x 32, then 32 x 16. Measured fused stage
-        // (16 x 16 -> 16 x 32): 56 x 56 ResNet-18 layer 18.5 -> 15.4 us, 28 x 28
-        // 22.8 -> 20.2 us, 14 x 14 39.1 -> 31.6 us; where the 16 x 16 blocks
-        // already give each CU one block (7 x 7, C = 512) the model keeps
-        // them (42 vs 61 us). 32 x 32 blocks of 16 waves (1) are slower than
-        // this model says on those layers and are only taken on request.
-        // WQ8_FUSED_WIDE = 0 (16 x 16), 1 (32 x 32), 2 (32 x 16) or 3
-        // (16 x 32) overrides.
-        auto busiest = [&](int64_t rt, int64_t rc) {
-            const int64_t nb = ((g.T + rt - 1) / rt) * ((g.Cout + rc - 1) / rc);
-            return ((nb + 255) / 256) * (rt + rc);
-        };
-        p->geo.fused_wide = 0;
-        if (m == 6 && d->group <= 64) {
-            const int64_t c0 = busiest(16, 16), c2 = busiest(32, 16), c3 = busiest(16, 32);
-            if (c3 <= c2 && c3 < c0) p->geo.fused_wide = 3;
-            else if (c2 < c0) p->geo.fused_wide = 2;
-        }
-        const char *wide = getenv("WQ8_FUSED_WIDE");
-        if (wide && atoi(wide) >= 0 && atoi(wide) <= 3)
-            p->geo.fused_wide = m == 6 && d->group <= 64 ? atoi(wide) : 0;
-    }
-    // stage-1 window rows: WQ8_STAGE1_ROWS = full or half forces a form (for
-    // tests); otherwise the launch picks half-row windows when the strips
-    // outnumber the blocks full windows let the GPU hold at once
-    {
-        const char *ov = getenv("WQ8_STAGE1_ROWS");
-        p->geo.s1_rows = ov && strcmp(ov, "full") == 0 ? 1 : ov && strcmp(ov, "half") == 0 ? 2 : 0;
-    }
+    // Kernel shapes. Every shape performs the same operations per output in
+    // the same order, so the results do not depend on them. 0 leaves the
+    // choice to the launch, which weighs the block count against the
+    // device's compute units; the descriptor may force one (tests, tuning).
+    if (d->stage1_rows < 0 || d->stage1_rows > 2)
+        return fail(WQ8_ERR_INVALID_ARG, "stage1_rows = %d: must be 0, 1 or 2", d->stage1_rows);
+    if (d->stage1_rows == 2 && g.in_quant != WQ8_INQ_FP32)
+        return fail(WQ8_ERR_UNSUPPORTED, "half-row windows need the fp32 input stage");
+    p->geo.s1_rows = d->stage1_rows;
+    if (d->fused_waves != 0 && d->fused_waves != 4 && d->fused_waves != 8 && d->fused_waves != 16)
+        return fail(WQ8_ERR_INVALID_ARG, "fused_waves = %d: must be 0, 4, 8 or 16", d->fused_waves);
+    if (d->fused_waves > 4 && m != 6)
+        return fail(WQ8_ERR_UNSUPPORTED, "8- and 16-wave fused blocks are built for F(6,3) only");
+    p->geo.fused_waves = d->fused_waves;
+    if (d->fused_block < 0 || d->fused_block > 4)
+        return fail(WQ8_ERR_INVALID_ARG, "fused_block = %d: must be 0..4", d->fused_block);
+    if (d->fused_block > 1 && !(m == 6 && d->group <= 64))
+        return fail(WQ8_ERR_UNSUPPORTED, "wide fused blocks are built for F(6,3) with G <= 64 only");
+    // Geo: -1 chosen at launch; 0 16 x 16; 1 32 x 32; 2 32 tiles x 16; 3 16 x 32
+    p->geo.fused_wide = d->fused_block - 1;
     return WQ8_OK;
 }
 

@@ -57,9 +57,9 @@ def assert_out(got, ref, what):
     return err
 
 
-def make_plan(L, d, xdt=torch.float32, ydt=None, algo="auto"):
+def make_plan(L, d, xdt=torch.float32, ydt=None, algo="auto", **shape):
     return q.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"], s_B=d["s_b"],
-                  s_G=d["s_g"], x_dtype=xdt, y_dtype=ydt, algo=algo)
+                  s_G=d["s_g"], x_dtype=xdt, y_dtype=ydt, algo=algo, **shape)
 
 
 def to_dev(a, dev):
@@ -207,52 +207,103 @@ def test_forward_is_deterministic(dev):
 FULL = list(WL.LAYERS.values())
 
 
-@pytest.mark.parametrize("algo", ["staged", "fused"])
-@pytest.mark.parametrize("L", FULL, ids=ids(FULL))
-def test_full_size_sampled(dev, L, algo):
-    """Full configuration, launched exactly as the benchmark launches it
-    (wq8_conv_forward with a plan-sized workspace). Transforms and codes are
-    compared in full; the Hadamard stage, Y codes and outputs at 192 sampled
-    (tile, co) pairs that the oracle evaluates one by one."""
-    print(f"\n[case] full {L.name} ({algo})", flush=True)
-    d = WL.make(L)
-    from oracle import transforms as T
-    Bt, Gm, At = T.transforms_f32(L.m, list(d["points"]), d["s_b"], d["s_g"])
-    oUq, osU = oracle.weights(L.m, d["w"], L.G, Gm)
-    oVq, osV = oracle.stage1(L.m, d["x"], L.pad, L.G, Bt)
-    plan = make_plan(L, d, algo=algo)
+def equalizing(m):
+    """Data-free equalizing scales written by tests/golden/make_equalized_scales.py
+    (which calls only oracle/)."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "equalized_scales.json")) as f:
+        e = json.load(f)[f"F({m},3)"]
+    return np.array(e["s_B"], np.float32), np.array(e["s_G"], np.float32)
+
+
+def scale_set(L, which):
+    n = L.m + 2
+    if which == "config":
+        return WL.make_scales(L)
+    if which == "standard":
+        return np.ones(n, np.float32), np.ones(n, np.float32)
+    if which == "equalizing":
+        return equalizing(L.m)
+    raise ValueError(which)
+
+
+def check_full(L, d, dev, schedules, stages=True):
+    """Every element of a full-size layer against the oracle, launched as
+    the benchmark launches it (wq8_conv_forward with a plan-sized
+    workspace): Uq, sU, Vq, sV in full; M (int8 GEMMs from the oracle's
+    codes) bit-exact; Yq, sY and the stage-3 output from the oracle's M;
+    the fused stages 2+3 from the oracle's codes; the whole forward for
+    each schedule in `schedules` against the oracle output at 1e-3 of its
+    RMS. Returns {schedule: max error / RMS}."""
+    ref = oracle.forward(L.m, d["x"], d["w"], L.pad, L.G, points=list(d["points"]), s_b=d["s_b"],
+                         s_g=d["s_g"], keep=True)
+    r = rms(ref["y"])
+    plan = make_plan(L, d)
     x = to_dev(d["x"], dev)
     Uq, sU = q.wq8_weights_prepare(plan, to_dev(d["w"], dev))
-    y = q.wq8_conv_forward(plan, x, Uq, sU, workspace=plan.empty_workspace(dev))
     Vq, sV = q.wq8_stage1(plan, x)
     torch.cuda.synchronize()
-    fu = assert_codes(Uq.cpu().numpy(), oUq, "Uq")
-    fv = assert_codes(Vq.cpu().numpy(), oVq, "Vq")
-    if fu == 0 and fv == 0:
-        assert np.array_equal(sU.cpu().numpy(), osU) and np.array_equal(sV.cpu().numpy(), osV)
-    r = np.random.default_rng([L.cfg_id, L.layer_idx, 99])
-    S = 192
-    pairs = np.stack([r.integers(0, plan.T, S), r.integers(0, L.Cout, S)], 1)
-    pairs[0] = (plan.T - 1, L.Cout - 1)          # the ragged corner
-    Ms, Yqs, sYs, ys = oracle.sampled(L.m, oVq, osV, oUq, osU, At, pairs)
-    M = q.wq8_stage2(plan, Vq, sV, Uq, sU)
-    torch.cuda.synchronize()
-    Mg = M.cpu().numpy()[:, pairs[:, 0], pairs[:, 1]].T
-    if fu == 0 and fv == 0:
-        assert np.array_equal(Mg, Ms)
-    yg = y.cpu().numpy()
-    tH, tW = -(-L.Ho // L.m), -(-L.Wo // L.m)
-    got, want = [], []
-    for s, (t, co) in enumerate(pairs):
-        img, ty, tx = t // (tH * tW), t // tW % tH, t % tW
-        blk = yg[img, co, ty * L.m:(ty + 1) * L.m, tx * L.m:(tx + 1) * L.m]
-        got.append(blk.reshape(-1))
-        want.append(ys[s][:blk.shape[0], :blk.shape[1]].reshape(-1))
-    got, want = np.concatenate(got), np.concatenate(want)
-    # RMS of the whole oracle output is estimated from the sampled tiles
-    err = float(np.max(np.abs(got.astype(np.float64) - want)))
-    assert err <= OUT_TOL * rms(want), f"max err {err:.3e} rms {rms(want):.3e}"
-    print(f"[case] full {L.name} ({algo}): sampled max err {err:.3e}", flush=True)
+    fu = assert_codes(Uq.cpu().numpy(), ref["Uq"], "Uq")
+    fv = assert_codes(Vq.cpu().numpy(), ref["Vq"], "Vq")
+    if fu == 0:
+        assert np.array_equal(sU.cpu().numpy(), ref["sU"]), "sU"
+    if fv == 0:
+        assert np.array_equal(sV.cpu().numpy(), ref["sV"]), "sV"
+    if stages:
+        oVq, osV = to_dev(ref["Vq"], dev), to_dev(ref["sV"], dev)
+        oUq, osU = to_dev(ref["Uq"], dev), to_dev(ref["sU"], dev)
+        ps = make_plan(L, d, algo="staged")
+        M = q.wq8_stage2(ps, oVq, osV, oUq, osU)
+        torch.cuda.synchronize()
+        assert np.array_equal(M.cpu().numpy(), ref["M"]), "M"
+        del M
+        y3, Yq, sY = q.wq8_stage3(ps, to_dev(ref["M"], dev), want_codes=True)
+        torch.cuda.synchronize()
+        assert_codes(Yq.cpu().numpy(), ref["Yq"], "Yq")
+        assert np.array_equal(sY.cpu().numpy(), ref["sY"]), "sY"
+        assert_out(y3.cpu().numpy(), ref["y"], "stage-3 output")
+        del y3, Yq, sY
+        y23 = q.wq8_stage23(make_plan(L, d, algo="fused"), oVq, osV, oUq, osU)
+        torch.cuda.synchronize()
+        assert_out(y23.cpu().numpy(), ref["y"], "fused stage-2+3 output")
+        del y23, oVq, osV, oUq, osU
+    errs, outs = {}, {}
+    for algo in schedules:
+        p2 = make_plan(L, d, algo=algo)
+        y = q.wq8_conv_forward(p2, x, Uq, sU, workspace=p2.empty_workspace(dev))
+        torch.cuda.synchronize()
+        outs[algo] = y.cpu().numpy()
+        errs[algo] = assert_out(outs[algo], ref["y"], f"forward ({algo})") / r
+    if "staged" in outs and "fused" in outs:
+        # identical codes; only the fp16 evaluation of A^T Yq A differs
+        diff = float(np.max(np.abs(outs["staged"].astype(np.float64) - outs["fused"])))
+        assert diff <= 2e-5 * r, f"fused vs staged forward: {diff / r:.2e} rms"
+    return errs
+
+
+@pytest.mark.parametrize("L", FULL, ids=ids(FULL))
+def test_full_size_elementwise(dev, L):
+    """Full configuration with its own scales, every element, both schedules
+    and the schedule the plan picks."""
+    print(f"\n[case] full {L.name} ({L.scales} scales)", flush=True)
+    d = WL.make(L)
+    errs = check_full(L, d, dev, ("staged", "fused", "auto"))
+    print(f"[case] full {L.name}: max err / rms " +
+          ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+
+
+@pytest.mark.parametrize("which", ["standard", "equalizing"])
+@pytest.mark.parametrize("L", FULL, ids=ids(FULL))
+def test_full_size_scale_sets(dev, L, which):
+    """Full configuration under the standard scales (S = I) and the
+    equalizing scales (F(6,3) s_B spans 0.13 to 24.8): codes and scales of
+    every stage, and the forward the plan picks, element by element."""
+    sb, sg = scale_set(L, which)
+    print(f"\n[case] full {L.name} ({which} scales)", flush=True)
+    d = dict(WL.make(L), s_b=sb, s_g=sg)
+    errs = check_full(L, d, dev, ("auto",))
+    print(f"[case] full {L.name} ({which}): max err / rms {errs['auto']:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("name", ["c2_f6_n32_c64_56x56_g64", "c4_f4_n2_c320_64x64_g64_pert",
@@ -286,17 +337,17 @@ def test_fused_output_transform_precision(dev, name):
     WL.small(WL.LAYERS["c5_f6_n8_c640_32x32_g128"], N=1, H=10, W=12, Cin=256, Cout=8),
     WL.small(WL.LAYERS["c5_f6_n8_c640_32x32_g32"], N=1, H=7, W=26, Cin=96, Cout=8),
 ], ids=lambda L: L.name)
-def test_stage1_window_rows(dev, monkeypatch, rows, L):
+def test_stage1_window_rows(dev, rows, L):
     """Stage 1 holds all n window rows in LDS, or half of them at a time
-    (the launch picks by how many strips the GPU can hold; WQ8_STAGE1_ROWS
-    forces one): both give the oracle's codes and scales bit for bit."""
-    monkeypatch.setenv("WQ8_STAGE1_ROWS", rows)
+    (the launch picks by how many strips the GPU can hold; the plan's
+    stage1_rows forces one): both give the oracle's codes and scales bit for
+    bit."""
     print(f"\n[case] stage-1 {rows} rows {L.name}", flush=True)
     d = WL.make(L)
     from oracle import transforms as T
     Bt = T.transforms_f32(L.m, list(d["points"]), d["s_b"], d["s_g"])[0]
     oVq, osV = oracle.stage1(L.m, d["x"], L.pad, L.G, Bt)
-    plan = make_plan(L, d)
+    plan = make_plan(L, d, stage1_rows={"full": 1, "half": 2}[rows])
     Vq, sV = q.wq8_stage1(plan, to_dev(d["x"], dev))
     torch.cuda.synchronize()
     assert np.array_equal(Vq.cpu().numpy(), oVq) and np.array_equal(sV.cpu().numpy(), osV)
@@ -309,17 +360,17 @@ def test_stage1_window_rows(dev, monkeypatch, rows, L):
     ("c5_f6_n8_c640_32x32_g32", dict(N=1, H=13, W=17, Cin=96, Cout=20)),
     ("c5_f6_n8_c1280_16x16_g128", dict(N=1, H=9, W=11, Cin=256, Cout=17)),
 ])
-def test_fused_block_shapes(dev, monkeypatch, waves, name, kw):
-    """The fused kernel splits a block's taps over 4, 8 or 16 waves (the plan
-    picks by block count; WQ8_FUSED_WAVES forces one): every shape gives the
-    oracle's result, for one and several quantization groups."""
-    monkeypatch.setenv("WQ8_FUSED_WAVES", str(waves))
+def test_fused_block_shapes(dev, waves, name, kw):
+    """The fused kernel splits a block's taps over 4, 8 or 16 waves (the
+    launch picks by block count; the plan's fused_waves forces one): every
+    shape gives the oracle's result, for one and several quantization
+    groups."""
     L = WL.small(WL.LAYERS[name], **kw)
     print(f"\n[case] fused waves={waves} {L.name} C={L.Cin}->{L.Cout} {L.H}x{L.W} G={L.G}", flush=True)
     d = WL.make(L)
     ref = oracle.forward(L.m, d["x"], d["w"], L.pad, L.G, points=list(d["points"]), s_b=d["s_b"],
                          s_g=d["s_g"])
-    plan = make_plan(L, d, algo="fused")
+    plan = make_plan(L, d, algo="fused", fused_waves=waves, fused_block=1)
     Uq, sU = q.wq8_weights_prepare(plan, to_dev(d["w"], dev))
     y = q.wq8_conv_forward(plan, to_dev(d["x"], dev), Uq, sU)
     torch.cuda.synchronize()
@@ -330,18 +381,16 @@ def test_fused_block_shapes(dev, monkeypatch, waves, name, kw):
     ("c2_f6_n32_c64_56x56_g64", dict(N=2, H=30, W=26, Cin=64, Cout=40)),
     ("c5_f6_n8_c640_32x32_g32", dict(N=1, H=13, W=17, Cin=96, Cout=20)),
 ])
-def test_fused_wave_counts_agree(dev, monkeypatch, name, kw):
+def test_fused_wave_counts_agree(dev, name, kw):
     """16 x 16 fused blocks of 4, 8 and 16 waves split the same per-pair work
     differently: their outputs agree bit for bit."""
     L = WL.small(WL.LAYERS[name], **kw)
     print(f"\n[case] fused wave counts {L.name}", flush=True)
     d = WL.make(L)
     x, w = to_dev(d["x"], dev), to_dev(d["w"], dev)
-    monkeypatch.setenv("WQ8_FUSED_WIDE", "0")
     outs = {}
     for waves in ("4", "8", "16"):
-        monkeypatch.setenv("WQ8_FUSED_WAVES", waves)
-        plan = make_plan(L, d, algo="fused")
+        plan = make_plan(L, d, algo="fused", fused_waves=int(waves), fused_block=1)
         Uq, sU = q.wq8_weights_prepare(plan, w)
         outs[waves] = q.wq8_conv_forward(plan, x, Uq, sU)
         torch.cuda.synchronize()
@@ -362,7 +411,7 @@ def test_fused_wave_counts_agree(dev, monkeypatch, name, kw):
     # two tiles in all (blocks almost all padding), one output channel past a block
     ("c2_f6_n32_c64_56x56_g64", dict(N=1, H=5, W=9, Cin=64, Cout=33), None, None),
 ])
-def test_fused_wide_blocks(dev, monkeypatch, name, kw, G, ydt, pad):
+def test_fused_wide_blocks(dev, name, kw, G, ydt, pad):
     """Wide fused blocks (32 x 32, 32 tiles x 16 channels, 16 tiles x 32
     channels; each tap's operands feed two or four MFMAs): the oracle's
     result, and bit for bit the output of the 16 x 16 blocks, whose per-pair
@@ -377,8 +426,7 @@ def test_fused_wide_blocks(dev, monkeypatch, name, kw, G, ydt, pad):
     x, w = to_dev(d["x"], dev), to_dev(d["w"], dev)
     outs = {}
     for wide in ("0", "1", "2", "3"):
-        monkeypatch.setenv("WQ8_FUSED_WIDE", wide)
-        plan = make_plan(L, d, ydt=ydt, algo="fused")
+        plan = make_plan(L, d, ydt=ydt, algo="fused", fused_block=int(wide) + 1)
         Uq, sU = q.wq8_weights_prepare(plan, w)
         outs[wide] = q.wq8_conv_forward(plan, x, Uq, sU)
         torch.cuda.synchronize()

@@ -39,7 +39,8 @@ def test_library_exports_every_declared_symbol():
 
 def _create(**kw):
     base = dict(m=6, points=None, s_B=None, s_G=None, group=64, N=1, Cin=64, Cout=64, H=16, W=16,
-                pad=1, x_dtype=0, y_dtype=0, algo=0, y_group=0, in_quant=0)
+                pad=1, x_dtype=0, y_dtype=0, algo=0, y_group=0, in_quant=0, stage1_rows=0,
+                fused_waves=0, fused_block=0)
     base.update(kw)
     keep = []
 
@@ -54,7 +55,7 @@ def _create(**kw):
                    arr(base["s_B"], C.c_float, np.float32), arr(base["s_G"], C.c_float, np.float32),
                    base["group"], base["N"], base["Cin"], base["Cout"], base["H"], base["W"],
                    base["pad"], base["x_dtype"], base["y_dtype"], base["algo"], base["y_group"],
-                   base["in_quant"])
+                   base["in_quant"], base["stage1_rows"], base["fused_waves"], base["fused_block"])
     h = C.c_void_p()
     st = B.wq8_plan_create(d, h)
     if st == 0:
@@ -83,6 +84,14 @@ def _create(**kw):
     (dict(s_G=[1, 1, 1, 1, math.inf, 1, 1, 1]), -1),
     (dict(s_B=[3e38] * 8, s_G=[1e-3] * 8), -1),
     (dict(N=4096, Cin=1024, Cout=1024, H=512, W=512, group=64), -2),
+    # kernel-shape fields: 0 = chosen at launch; out of range -1; not built -2
+    (dict(stage1_rows=1), 0), (dict(stage1_rows=2), 0), (dict(stage1_rows=3), -1),
+    (dict(stage1_rows=-1), -1), (dict(stage1_rows=2, in_quant=1), -2),
+    (dict(fused_waves=4), 0), (dict(fused_waves=8), 0), (dict(fused_waves=16), 0),
+    (dict(fused_waves=6), -1), (dict(fused_waves=8, m=4), -2), (dict(fused_waves=4, m=4), 0),
+    (dict(fused_block=1), 0), (dict(fused_block=4), 0), (dict(fused_block=5), -1),
+    (dict(fused_block=-1), -1), (dict(fused_block=2, m=4), -2),
+    (dict(fused_block=3, group=128, Cin=128), -2), (dict(fused_block=1, group=128, Cin=128), 0),
 ])
 def test_plan_validation(kw, status):
     assert _create(**kw) == status
@@ -179,3 +188,83 @@ def test_plan_reports_schedule():
     assert not B.Plan(6, 32, 64, 64, 56, 56, 1, 64, algo="staged").fused
     st = B.Plan(6, 32, 64, 64, 56, 56, 1, 64, algo="staged")
     assert small.workspace_bytes < st.workspace_bytes            # no M buffer when fused
+
+
+def test_no_environment_reads_in_library_sources():
+    """Kernel shapes come from the descriptor only: the library reads no
+    process environment."""
+    csrc = os.path.join(ROOT, "quantized_convolution_amd", "csrc")
+    for f in os.listdir(csrc):
+        src = open(os.path.join(csrc, f)).read()
+        assert "getenv" not in src, f
+
+
+def _tiny_plan(**kw):
+    return B.Plan(6, 1, 64, 16, 9, 9, 1, 64, algo="staged", **kw)
+
+
+def _cases(plan):
+    """(callable, what) pairs, each with one bad buffer; all others are good
+    CPU tensors (so the only failure a correct check can report before the
+    device check is the planted one)."""
+    f32, i8 = torch.float32, torch.int8
+    x = torch.zeros(plan.x_shape)
+    Uq, sU = torch.zeros(plan.uq_shape, dtype=i8), torch.zeros(plan.su_shape)
+    Vq, sV = torch.zeros(plan.vq_shape, dtype=i8), torch.zeros(plan.sv_shape)
+    M = torch.zeros(plan.m_shape)
+    y = torch.zeros(plan.y_shape)
+    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8)
+    return [
+        (lambda: B.wq8_conv_forward(plan, x.double(), Uq, sU, y, ws), "x must be"),
+        (lambda: B.wq8_conv_forward(plan, x[:, :, :8], Uq, sU, y, ws), "x must have shape"),
+        (lambda: B.wq8_conv_forward(plan, x, Uq[:, :8], sU, y, ws), "Uq must have shape"),
+        (lambda: B.wq8_conv_forward(plan, x, Uq.to(torch.uint8), sU, y, ws), "Uq must be"),
+        (lambda: B.wq8_conv_forward(plan, x, Uq, sU.double(), y, ws), "sU must be"),
+        (lambda: B.wq8_conv_forward(plan, x, Uq, sU, y.to(torch.bfloat16), ws), "y must be"),
+        (lambda: B.wq8_conv_forward(plan, x, Uq, sU, y[:, :, :1], ws), "y must have shape"),
+        (lambda: B.wq8_conv_forward(plan, x, Uq, sU, y, ws[:-1]), "workspace holds"),
+        (lambda: B.wq8_conv_forward(plan, x, Uq, sU, y, ws), "must be on a GPU"),
+        (lambda: B.wq8_stage1(plan, x, Vq[:, :1], sV), "Vq must have shape"),
+        (lambda: B.wq8_stage1(plan, x, Vq, sV.to(f32)[:, :, :0]), "sV must have shape"),
+        (lambda: B.wq8_stage2(plan, Vq, sV, Uq, sU, M.double()), "M must be"),
+        (lambda: B.wq8_stage2(plan, Vq, sV, Uq, sU, M[:1]), "M must have shape"),
+        (lambda: B.wq8_stage2_i32(plan, Vq, Uq, torch.zeros(1, dtype=torch.int32)), "P must have shape"),
+        (lambda: B.wq8_stage3(plan, M[:, :1], y), "M must have shape"),
+        (lambda: B.wq8_stage3(plan, M, y, Yq=torch.zeros(1, dtype=i8),
+                              sY=torch.zeros((plan.T, plan.Cout))), "Yq must have shape"),
+        (lambda: B.wq8_stage23(plan, Vq, sV, Uq, sU, y.t() if y.dim() == 2 else y[:, :, :, :1]),
+         "y must have shape"),
+        (lambda: B.wq8_stage23(plan, Vq, sV, Uq, sU, torch.zeros(plan.y_shape).transpose(2, 3)),
+         "y must be contiguous"),
+        (lambda: B.wq8_weights_prepare(plan, torch.zeros((16, 64, 3, 3)), Uq, sU[..., :0]), "sU must have shape"),
+        (lambda: B.wq8_direct_conv(plan, torch.zeros((1, 9, 9, 64), dtype=i8), torch.zeros((1, 9, 9, 1)),
+                                   torch.zeros((9, 16, 64), dtype=i8), torch.zeros((9, 16, 2)), y),
+         "sW must have shape"),
+        (lambda: B.wq8_direct_forward(plan, x, torch.zeros((9, 16, 64), dtype=i8), torch.zeros((9, 16, 1)), y,
+                                      torch.zeros(8, dtype=torch.uint8)), "workspace holds"),
+        (lambda: B.wq8_conv_forward(plan, x, Uq, sU, "not a tensor", ws), "y must be a torch tensor"),
+    ]
+
+
+@pytest.mark.parametrize("k", range(22))
+def test_binding_rejects_bad_buffers_before_launch(k):
+    """Every wrapper checks dtype, shape, contiguity and device of every
+    buffer against the plan and raises ValueError before any call into the
+    library (the kernels size their accesses from the plan, not from the
+    tensors)."""
+    plan = _tiny_plan()
+    cases = _cases(plan)
+    assert len(cases) == 22
+    fn, what = cases[k]
+    with pytest.raises(ValueError, match=what):
+        fn()
+
+
+@pytest.mark.skipif(not HAS_GPU, reason="needs two kinds of device")
+def test_binding_rejects_mixed_devices():
+    plan = _tiny_plan()
+    x = torch.zeros(plan.x_shape, device="cuda")
+    Uq = torch.zeros(plan.uq_shape, dtype=torch.int8)
+    sU = torch.zeros(plan.su_shape, device="cuda")
+    with pytest.raises(ValueError, match="must be on a GPU"):
+        B.wq8_conv_forward(plan, x, Uq, sU)
