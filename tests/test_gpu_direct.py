@@ -97,6 +97,15 @@ def test_direct_rejects_small_workspace(dev):
     x = torch.zeros((L.N, L.Cin, L.H, L.W), device=dev)
     Wq, sW = q.wq8_direct_weights_prepare(plan, torch.zeros((L.Cout, L.Cin, 3, 3), device=dev))
     ws = torch.empty(plan.direct_workspace_bytes - 256, dtype=torch.uint8, device=dev)
-    with pytest.raises(q.Wq8Error) as e:
-        q.wq8_direct_forward(plan, x, Wq, sW, workspace=ws)
-    assert e.value.status == -4
+    y = plan.empty_output(dev)
+    # the binding refuses before calling the library ...
+    with pytest.raises(ValueError, match="workspace"):
+        q.wq8_direct_forward(plan, x, Wq, sW, y=y, workspace=ws)
+    # ... and so does the library itself, called directly through the C ABI
+    import ctypes as C
+    from quantized_convolution_amd import binding as B
+    st = B.load().wq8_direct_forward(plan.handle, C.c_void_p(x.data_ptr()), C.c_void_p(Wq.data_ptr()),
+                                     C.c_void_p(sW.data_ptr()), C.c_void_p(y.data_ptr()),
+                                     C.c_void_p(ws.data_ptr()), C.c_size_t(ws.numel()),
+                                     C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == -4
