@@ -183,6 +183,23 @@ wq8_status wq8_conv_forward(const wq8_plan *plan, const void *x, const int8_t *U
                             const float *sU, void *y, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* wq8_conv_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The workspace is a device array built into
+ * the library, WQ8_NOALLOC_MAX_WORKSPACE bytes on every GPU the library runs
+ * on, held from module load until the process ends; this call allocates
+ * nothing. Its device address is looked up once per device, on the first call
+ * with that device current. Plans whose forward needs a larger workspace
+ * (wq8_plan_query) get WQ8_ERR_WORKSPACE_TOO_SMALL and nothing is launched.
+ * All calls on one GPU share that GPU's array: calls that overlap in time on
+ * one GPU (different streams, or several host threads) race and give wrong
+ * results; serialise them. The array keeps the last call's contents; no stage
+ * reads workspace bytes it has not written in the same call. Results are bit
+ * for bit those of wq8_conv_forward. */
+#define WQ8_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+wq8_status wq8_conv_forward_noalloc(const wq8_plan *plan, const void *x, const int8_t *Uq,
+                                    const float *sU, void *y, void *stream);
+
 /* Individual stages with the layouts above (for parity checks and profiling). */
 wq8_status wq8_stage1(const wq8_plan *plan, const void *x, int8_t *Vq, float *sV,
                       void *stream);

@@ -45,7 +45,10 @@ EXPORTS = ("wq8_plan_create", "wq8_plan_destroy", "wq8_plan_query", "wq8_plan_ma
            "wq8_weights_prepare", "wq8_conv_forward", "wq8_stage1", "wq8_stage2",
            "wq8_stage2_i32", "wq8_stage3", "wq8_stage23", "wq8_direct_query",
            "wq8_direct_weights_prepare", "wq8_direct_quantize_x", "wq8_direct_conv",
-           "wq8_direct_forward", "wq8_status_string", "wq8_last_error")
+           "wq8_direct_forward", "wq8_conv_forward_noalloc", "wq8_status_string", "wq8_last_error")
+
+# bytes of the device array wq8_conv_forward_noalloc uses as its workspace
+NOALLOC_MAX_WORKSPACE = 64 << 20
 
 _lib = None
 
@@ -79,6 +82,7 @@ def load(path: str = LIB_PATH):
     lib.wq8_direct_quantize_x.argtypes = [P, P, P, P, P]
     lib.wq8_direct_conv.argtypes = [P, P, P, P, P, P, P]
     lib.wq8_direct_forward.argtypes = [P, P, P, P, P, P, S, P]
+    lib.wq8_conv_forward_noalloc.argtypes = [P, P, P, P, P, P]
     lib.wq8_status_string.argtypes = [i]
     lib.wq8_status_string.restype = C.c_char_p
     lib.wq8_last_error.argtypes = []
@@ -312,6 +316,20 @@ def wq8_conv_forward(plan: Plan, x, Uq, sU, y=None, workspace=None, stream=None)
     nbytes = workspace.numel() * workspace.element_size()
     b.call(load().wq8_conv_forward, plan.handle, _ptr(x), _ptr(Uq), _ptr(sU), _ptr(y),
            _ptr(workspace), C.c_size_t(nbytes), stream=stream)
+    return y
+
+
+def wq8_conv_forward_noalloc(plan: Plan, x, Uq, sU, y, stream=None):
+    """The forward on the library's built-in workspace (no device allocation
+    by the library; y is the caller's). Calls that overlap on one GPU race."""
+    b = _Bufs()
+    _check_x(plan, b, x)
+    _check_weights(plan, b, Uq, sU)
+    b(y, "y", plan.y_dtype, plan.y_shape)
+    if y.data_ptr() == x.data_ptr():
+        raise ValueError("x and y must not overlap")
+    b.call(load().wq8_conv_forward_noalloc, plan.handle, _ptr(x), _ptr(Uq), _ptr(sU), _ptr(y),
+           stream=stream)
     return y
 
 

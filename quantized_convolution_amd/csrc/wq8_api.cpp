@@ -30,6 +30,33 @@ wq8_status need(const void *p, const char *name) {
 
 }  // namespace
 
+namespace wq8 {
+
+wq8_status forward_launch(const wq8_plan *p, const void *x, const int8_t *Uq, const float *sU,
+                          void *y, void *workspace, void *stream) {
+    char *ws = (char *)workspace;
+    int8_t *Vq = (int8_t *)(ws + p->off_vq);
+    float *sV = (float *)(ws + p->off_sv);
+    float *M = (float *)(ws + p->off_m);
+    WQ8_TRY(launch_stage1(p->geo, p->mats, p->xdt, x, Vq, sV, stream));
+    if (p->fused) return launch_fused23(p->geo, p->mats, p->ydt, Vq, sV, Uq, sU, y, stream);
+    WQ8_TRY(launch_stage2(p->geo, Vq, sV, Uq, sU, M, nullptr, stream));
+    return launch_stage3(p->geo, p->mats, p->ydt, M, y, nullptr, nullptr, stream);
+}
+
+wq8_status check_forward_args(const wq8_plan *p, const void *x, const int8_t *Uq, const float *sU,
+                              const void *y) {
+    if (!p) return fail(WQ8_ERR_INVALID_ARG, "null plan");
+    WQ8_NEED(x);
+    WQ8_NEED(Uq);
+    WQ8_NEED(sU);
+    WQ8_NEED(y);
+    if (x == y) return fail(WQ8_ERR_INVALID_ARG, "x and y must not overlap");
+    return WQ8_OK;
+}
+
+}  // namespace wq8
+
 extern "C" {
 
 wq8_status wq8_weights_prepare(const wq8_plan *p, const float *w, int8_t *Uq, float *sU,
@@ -55,14 +82,7 @@ wq8_status wq8_conv_forward(const wq8_plan *p, const void *x, const int8_t *Uq, 
         return fail(WQ8_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
                     p->ws_bytes);
     if (x == y) return fail(WQ8_ERR_INVALID_ARG, "x and y must not overlap");
-    char *ws = (char *)workspace;
-    int8_t *Vq = (int8_t *)(ws + p->off_vq);
-    float *sV = (float *)(ws + p->off_sv);
-    float *M = (float *)(ws + p->off_m);
-    WQ8_TRY(launch_stage1(p->geo, p->mats, p->xdt, x, Vq, sV, stream));
-    if (p->fused) return launch_fused23(p->geo, p->mats, p->ydt, Vq, sV, Uq, sU, y, stream);
-    WQ8_TRY(launch_stage2(p->geo, Vq, sV, Uq, sU, M, nullptr, stream));
-    return launch_stage3(p->geo, p->mats, p->ydt, M, y, nullptr, nullptr, stream);
+    return forward_launch(p, x, Uq, sU, y, workspace, stream);
 }
 
 wq8_status wq8_stage1(const wq8_plan *p, const void *x, int8_t *Vq, float *sV, void *stream) {

@@ -66,6 +66,14 @@ wq8_status launch_fused23(const Geo &g, const Mats &mt, wq8_dtype ydt, const int
                           const float *sV, const int8_t *Uq, const float *sU, void *y,
                           void *stream);
 
+// The forward's kernels on a workspace laid out as the plan says (Vq | sV |
+// M); arguments already checked.
+wq8_status forward_launch(const wq8_plan *p, const void *x, const int8_t *Uq, const float *sU,
+                          void *y, void *workspace, void *stream);
+// The forward's pointer checks (null, 16-byte alignment, x != y).
+wq8_status check_forward_args(const wq8_plan *p, const void *x, const int8_t *Uq, const float *sU,
+                              const void *y);
+
 // Group-wise W8A8 direct convolution (wq8_direct.hip), the non-Winograd
 // baseline: weights Wq [9][Cout][Cin] / sW [9][Cout][Cin/G], activation codes
 // Xq [N][H][W][Cin] / sX [N][H][W][Cin/G].
