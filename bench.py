@@ -1,14 +1,18 @@
-"""Benchmark: quantized Winograd F(6,3) conv layer on one MI355X.
+"""Benchmark: quantized Winograd F(m,3) conv layers on one MI355X.
 
-Workload: the ResNet-18-shaped 3x3 layer (N=32, Cin=Cout=64, 56x56, pad 1,
-group 64, seeded exp(U(-1/2,1/2)) transform scales), synthetic seeded inputs.
-A step is one whole forward (input transform + int8 Hadamard GEMMs + output
-transform) with inputs and prepared weights resident in HBM; the weight
-transform is done once before timing.
+Workload (the headline): the largest configuration, a deep UNet-shaped 3x3
+layer, F(6,3), N=8, Cin=Cout=1280, 16x16, pad 1, group 32, Student-t(3)
+activations with 1 % of the channels x20, N(0, 0.02^2) weights, seeded
+exp(U(-1/2,1/2)) transform scales; synthetic seeded inputs. A step is one
+whole forward (input transform + int8 Hadamard GEMMs + output transform) with
+inputs and prepared weights resident in HBM; the weight transform is done
+once before timing. K steps are captured in one HIP graph and replayed
+between two HIP events on the launch stream.
 
-Prints one JSON line: direct-conv-equivalent int8 TOPS, the per-kernel
-roofline of the dominant kernel (HIP events around each stage's kernel on the
-stream it runs on), and the CPU oracle timed on the host for comparison.
+Prints one JSON line: direct-conv-equivalent int8 TOPS, the roofline of the
+dominant kernel (each kernel's own launches, captured and replayed the same
+way), per-layer records for every configuration, SQNR per scale set, and the
+CPU oracle timed on the host for comparison.
 """
 from __future__ import annotations
 
@@ -32,6 +36,7 @@ sys.path.insert(0, ROOT)
 import quantized_convolution_amd as q  # noqa: E402
 from quantized_convolution_amd import workloads as WL  # noqa: E402
 
+HEADLINE = "c5_f6_n8_c1280_16x16_g32"  # the largest configuration (bytes moved per layer)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POP/s)
 KERNEL_SRC = os.path.join(ROOT, "quantized_convolution_amd", "csrc", "wq8_kernels.hip")
@@ -116,7 +121,15 @@ def traffic_summary(layer, fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mi
 
     fr, wr = copy_factor(cfetch_dir, "FETCH_SIZE"), copy_factor(cwrite_dir, "WRITE_SIZE")
     out = {"kernel_source_sha": kernel_source_sha(), "copy_probe_mib": copy_mib,
-           "fetch_factor": round(fr, 4), "write_factor": round(wr, 4), "layers": {layer: {}}}
+           "fetch_factor": round(fr, 4), "write_factor": round(wr, 4), "layers": {}}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            old = json.load(f)
+        if old.get("kernel_source_sha") == out["kernel_source_sha"]:
+            out["layers"] = old.get("layers", {})  # other layers taken on the same code
+    except (OSError, ValueError):
+        pass
+    out["layers"][layer] = {}
     fetch, write = _pmc_rows(fetch_dir, "FETCH_SIZE"), _pmc_rows(write_dir, "WRITE_SIZE")
     lines = ["| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (scaled) |",
              "|---|---|---|---|---|"]
@@ -163,6 +176,8 @@ def stage_bytes(L, plan):
 
 
 def time_events(fn, iters, stream):
+    """Average ms per call of `iters` eagerly launched calls (each call goes
+    through the Python binding, so short kernels measure the host instead)."""
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -173,16 +188,47 @@ def time_events(fn, iters, stream):
     return start.elapsed_time(end) / iters  # ms
 
 
-def time_each(fn, iters, stream, before=None):
-    """Per-call times (ms) from an event pair around each call; `before` runs
-    between the calls, outside the timed pairs."""
+def capture(fn, reps):
+    """A HIP graph of `reps` calls of fn (every kernel the calls launch, in
+    order, on the capture stream; nothing else is recorded)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # first call outside the graph: per-device lookups happen here
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps, stream, replays=1):
+    """ms per call: `replays` replays of a graph of `reps` calls between two
+    events on `stream`; the kernels run back to back with no host launch in
+    between."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(replays):
+        g.replay()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / (reps * replays)
+
+
+def time_cold(g, n, stream, flush):
+    """ms of each of n replays of a one-call graph, each after a 512 MiB fill
+    that evicts the 256 MB Infinity Cache and the L2s (the fill also keeps the
+    GPU busy while the replay is enqueued)."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(iters)]
+           for _ in range(n)]
     for a, b in evs:
-        if before is not None:
-            before()
+        flush.fill_(1.0)
         a.record(stream)
-        fn()
+        g.replay()
         b.record(stream)
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in evs]
@@ -231,13 +277,25 @@ def cpu_baseline(L, d, min_seconds=10.0):
             "direct_f64_ms": round(td * 1e3, 1)}
 
 
-def accuracy(L, d, dev, images=4):
-    """Output SQNR (dB) of the GPU forward against a float64 CPU convolution
-    (torch), on the first `images` images, for the timed scales, standard
-    scales (S = I) and equalising scales."""
+def scale_sets(L, d):
+    """Transform scales the accuracy report covers: the timed workload's
+    (seeded exp(U(-1/2, 1/2)) or identity), standard (S = I), the data-free
+    equalizing set, and the learned set for this m when one is recorded."""
     from quantized_convolution_amd import scales as S
 
     n = L.m + 2
+    sets = {"timed_scales": (d["s_b"], d["s_g"]), "standard_S_I": ([1.0] * n, [1.0] * n),
+            "equalizing": S.equalizing_scales(L.m, list(d["points"]))}
+    learned = S.recorded_learned_scales(L.m)
+    if learned is not None:
+        sets["learned"] = learned
+    return sets
+
+
+def accuracy(L, d, dev, images):
+    """Output SQNR (dB) of the GPU forward against a float64 CPU convolution
+    (torch), on the first `images` images, for each scale set; the literal
+    input-stage readings for the timed and equalizing scales."""
     x = torch.from_numpy(d["x"][:images]).to(dev)
     w = torch.from_numpy(d["w"]).to(dev)
     ref = torch.nn.functional.conv2d(torch.from_numpy(d["x"][:images]).double(),
@@ -245,8 +303,9 @@ def accuracy(L, d, dev, images=4):
     out = {}
     for iq in ("fp32", "int_tensor", "int_row"):
         row = {}
-        for name, (b, g) in {"timed_scales": (d["s_b"], d["s_g"]), "standard_S_I": ([1.0] * n, [1.0] * n),
-                             "equalizing": S.equalizing_scales(L.m, list(d["points"]))}.items():
+        for name, (b, g) in scale_sets(L, d).items():
+            if iq != "fp32" and name not in ("timed_scales", "equalizing"):
+                continue
             plan = q.Plan(L.m, images, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"], s_B=b,
                           s_G=g, in_quant=iq)
             Uq, sU = q.wq8_weights_prepare(plan, w)
@@ -259,10 +318,31 @@ def accuracy(L, d, dev, images=4):
                            "row) and input patches quantized, integer transform"}
 
 
-def run_layer(L, algo, steps, warmup, dev):
-    d = WL.make(L)
-    plan = q.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"],
-                  s_B=d["s_b"], s_G=d["s_g"], algo=algo)
+def mfma_report(L, plan, us, bytes_):
+    """int8 Hadamard work of a stage-2 (or fused) launch against the MFMA
+    peak, and the ceiling its arithmetic intensity allows from HBM:
+    min(1, AI * BW / peak)."""
+    hop = 2 * plan.n ** 2 * plan.T * L.Cin * L.Cout
+    tops = hop / (us * 1e-6) / 1e12
+    ceiling = min(1.0, hop / bytes_ * HBM_PEAK_GBS * 1e9 / (INT8_PEAK_TOPS * 1e12))
+    frac = tops / INT8_PEAK_TOPS
+    return {"int8_TOPS": round(tops, 2), "mfma_frac": round(frac, 5),
+            "mfma_ceiling": round(ceiling, 5), "of_ceiling": round(frac / ceiling, 4)}
+
+
+def make_plan(L, d, algo="auto", **kw):
+    return q.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"],
+                  s_B=d["s_b"], s_G=d["s_g"], algo=algo, **kw)
+
+
+def run_layer(L, algo, steps, warmup, dev, d=None, cold_reps=20, extras=False):
+    """One layer: the forward (K steps captured in one HIP graph and
+    replayed between two events; the same K steps eagerly launched for
+    comparison), each kernel on its own (its stage entry point captured
+    `iters` times), warm and after a cache flush. extras: the literal input
+    stage and the W8A8 direct baseline on the same workload."""
+    d = WL.make(L) if d is None else d
+    plan = make_plan(L, d, algo)
     x = torch.from_numpy(d["x"]).to(dev)
     w = torch.from_numpy(d["w"]).to(dev)
     Uq, sU = q.wq8_weights_prepare(plan, w)
@@ -276,72 +356,120 @@ def run_layer(L, algo, steps, warmup, dev):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    g = capture(step, steps)
+    g.replay()  # warm replay
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = time_events(step, steps, stream)
+    ms = time_graph(g, steps, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    # per-step distribution, caches warm, and cold: a 512 MiB fill before each
-    # step evicts the 256 MB Infinity Cache (and the L2s)
-    hot = time_each(step, min(steps, 100), stream)
+    eager = time_events(step, steps, stream)
+    del g
     flush = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
-    cold = time_each(step, 20, stream, before=lambda: flush.fill_(1.0))
-    del flush
+    g1 = capture(step, 1)
+    cold = time_cold(g1, cold_reps, stream, flush)
+    del g1
 
     # per-kernel durations: each stage entry point launches exactly the kernel
-    # the forward launches, with the same grid, on the same stream
-    n2 = plan.n ** 2
-    Vq = torch.empty((n2, plan.T, L.Cin), dtype=torch.int8, device=dev)
-    sV = torch.empty((n2, plan.T, plan.ng), dtype=torch.float32, device=dev)
-    iters = max(20, steps // 2)
-    k_ms = {"stage1": time_events(lambda: q.wq8_stage1(plan, x, Vq, sV), iters, stream)}
+    # the forward launches, with the same grid
+    Vq = torch.empty(plan.vq_shape, dtype=torch.int8, device=dev)
+    sV = torch.empty(plan.sv_shape, dtype=torch.float32, device=dev)
+    q.wq8_stage1(plan, x, Vq, sV)
+    calls = {"stage1": lambda: q.wq8_stage1(plan, x, Vq, sV)}
     if plan.fused:
-        k_ms["stage23"] = time_events(lambda: q.wq8_stage23(plan, Vq, sV, Uq, sU, y), iters, stream)
+        calls["stage23"] = lambda: q.wq8_stage23(plan, Vq, sV, Uq, sU, y)
     else:
-        M = torch.empty((n2, plan.T, L.Cout), dtype=torch.float32, device=dev)
-        k_ms["stage2"] = time_events(lambda: q.wq8_stage2(plan, Vq, sV, Uq, sU, M), iters, stream)
-        k_ms["stage3"] = time_events(lambda: q.wq8_stage3(plan, M, y), iters, stream)
+        M = torch.empty(plan.m_shape, dtype=torch.float32, device=dev)
+        calls["stage2"] = lambda: q.wq8_stage2(plan, Vq, sV, Uq, sU, M)
+        calls["stage3"] = lambda: q.wq8_stage3(plan, M, y)
+    iters = max(20, steps // 2)
+    k_ms, k_cold = {}, {}
+    for k, fn in calls.items():
+        gk = capture(fn, iters)
+        gk.replay()
+        k_ms[k] = time_graph(gk, iters, stream)
+        del gk
+        gk = capture(fn, 1)
+        k_cold[k] = statistics.median(time_cold(gk, cold_reps, stream, flush))
+        del gk
+    del flush
     nbytes = stage_bytes(L, plan)
-    hop = 2 * n2 * plan.T * L.Cin * L.Cout
     stages = {}
     for k, v in k_ms.items():
         gbs = nbytes[k] / (v * 1e-3) / 1e9
-        stages[k] = {"us": round(v * 1e3, 2), "GB_s": round(gbs, 1),
-                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        cgbs = nbytes[k] / (k_cold[k] * 1e-3) / 1e9
+        stages[k] = {"us": round(v * 1e3, 2), "cold_us": round(k_cold[k] * 1e3, 2),
+                     "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "cold_hbm_frac": round(cgbs / HBM_PEAK_GBS, 4), "bytes": nbytes[k]}
         if k in ("stage2", "stage23"):
-            stages[k]["int8_TOPS"] = round(hop / (v * 1e-3) / 1e12, 2)
-            stages[k]["mfma_frac"] = round(hop / (v * 1e-3) / 1e12 / INT8_PEAK_TOPS, 5)
+            stages[k]["mfma"] = mfma_report(L, plan, v * 1e3, nbytes[k])
+            stages[k]["mfma_cold"] = mfma_report(L, plan, k_cold[k] * 1e3, nbytes[k])
+    out = dict(plan=plan, d=d, ms=ms, eager_ms=eager, wall=wall, stages=stages, k_ms=k_ms,
+               nbytes=nbytes, tops=L.direct_ops() / (ms * 1e-3) / 1e12,
+               cold=(statistics.median(cold), min(cold)))
+    if not extras:
+        return out
     # the literal input stage (quantized B^T and input patch, integer
     # transform): its stage-1 kernel and whole forward on the same workload
     lit = {}
     for iq in ("int_tensor", "int_row"):
-        pl = q.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"], s_B=d["s_b"],
-                    s_G=d["s_g"], algo=algo, in_quant=iq)
-        s1 = time_events(lambda: q.wq8_stage1(pl, x, Vq, sV), iters, stream)
-        fw = time_events(lambda: q.wq8_conv_forward(pl, x, Uq, sU, y=y, workspace=ws), iters, stream)
+        pl = make_plan(L, d, algo, in_quant=iq)
+        gs = capture(lambda: q.wq8_stage1(pl, x, Vq, sV), iters)
+        s1 = time_graph(gs, iters, stream)
+        del gs
+        gf = capture(lambda: q.wq8_conv_forward(pl, x, Uq, sU, y=y, workspace=ws), iters)
+        fw = time_graph(gf, iters, stream)
+        del gf
         lit[iq] = {"stage1_us": round(s1 * 1e3, 2),
                    "stage1_hbm_frac": round(nbytes["stage1"] / (s1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                    "forward_us": round(fw * 1e3, 2),
                    "TOPS": round(L.direct_ops() / (fw * 1e-3) / 1e12, 2)}
+    out["literal"] = lit
     # the non-Winograd baseline on the same layer: group-wise W8A8 direct conv
     Wq, sW = q.wq8_direct_weights_prepare(plan, w)
     dws = torch.empty(plan.direct_workspace_bytes, dtype=torch.uint8, device=dev)
-    for _ in range(3):
-        q.wq8_direct_forward(plan, x, Wq, sW, y=y, workspace=dws)
-    d_ms = time_events(lambda: q.wq8_direct_forward(plan, x, Wq, sW, y=y, workspace=dws), iters, stream)
     Xq, sX = q.wq8_direct_quantize_x(plan, x)
-    dq_ms = time_events(lambda: q.wq8_direct_quantize_x(plan, x, Xq, sX), iters, stream)
-    dc_ms = time_events(lambda: q.wq8_direct_conv(plan, Xq, sX, Wq, sW, y=y), iters, stream)
-    direct = {"us": round(d_ms * 1e3, 2), "quantize_x_us": round(dq_ms * 1e3, 2),
-              "conv_us": round(dc_ms * 1e3, 2), "TOPS": round(L.direct_ops() / (d_ms * 1e-3) / 1e12, 2),
-              "winograd_speedup": round(d_ms / ms, 3)}
-    del dws, Xq, sX
+    dn = max(5, iters // 4)
+    res = {}
+    for key, fn in (("forward", lambda: q.wq8_direct_forward(plan, x, Wq, sW, y=y, workspace=dws)),
+                    ("quantize_x", lambda: q.wq8_direct_quantize_x(plan, x, Xq, sX)),
+                    ("conv", lambda: q.wq8_direct_conv(plan, Xq, sX, Wq, sW, y=y))):
+        gd = capture(fn, dn)
+        res[key] = time_graph(gd, dn, stream)
+        del gd
+    out["direct"] = {"us": round(res["forward"] * 1e3, 2), "quantize_x_us": round(res["quantize_x"] * 1e3, 2),
+                     "conv_us": round(res["conv"] * 1e3, 2),
+                     "TOPS": round(L.direct_ops() / (res["forward"] * 1e-3) / 1e12, 2),
+                     "winograd_speedup": round(res["forward"] / ms, 3)}
+    return out
 
-    dom = max(k_ms, key=k_ms.get)
-    achieved = nbytes[dom] / (k_ms[dom] * 1e-3) / 1e9
-    return dict(plan=plan, d=d, ms=ms, wall=wall, stages=stages, dom=dom, achieved=achieved,
-                nbytes=nbytes, tops=L.direct_ops() / (ms * 1e-3) / 1e12, direct=direct, literal=lit,
-                hot=(statistics.median(hot), min(hot)), cold=(statistics.median(cold), min(cold)))
+
+def layer_entry(L, r):
+    """Per-layer record: forward time and throughput, each kernel warm and
+    cold against HBM, and the Hadamard stage against int8 MFMA."""
+    return {"schedule": "fused" if r["plan"].fused else "staged", "tiles": r["plan"].T,
+            "forward_us": round(r["ms"] * 1e3, 2), "TOPS": round(r["tops"], 2),
+            "cold_forward_us": round(r["cold"][0] * 1e3, 2),
+            "cold_TOPS": round(L.direct_ops() / (r["cold"][0] * 1e-3) / 1e12, 2),
+            "eager_forward_us": round(r["eager_ms"] * 1e3, 2), "stages": r["stages"]}
+
+
+def profile_run(L, algo, steps, dev):
+    """Only the forward of one layer, `steps` times (eager launches, one
+    process): the command rocprofv3 traces or counts for the summaries under
+    profiles/."""
+    d = WL.make(L)
+    plan = make_plan(L, d, algo)
+    x = torch.from_numpy(d["x"]).to(dev)
+    Uq, sU = q.wq8_weights_prepare(plan, torch.from_numpy(d["w"]).to(dev))
+    y = plan.empty_output(dev)
+    ws = plan.empty_workspace(dev)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        q.wq8_conv_forward(plan, x, Uq, sU, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_run": L.name, "schedule": "fused" if plan.fused else "staged",
+                      "forwards": steps}), flush=True)
 
 
 def main():
@@ -349,16 +477,20 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--layer", default=WL.BENCH_LAYER, choices=sorted(WL.LAYERS))
+    ap.add_argument("--layer", default=HEADLINE, choices=sorted(WL.LAYERS))
     ap.add_argument("--algo", default="auto", choices=["auto", "staged", "fused"])
     ap.add_argument("--sweep", action="store_true",
                     help="one line per layer and schedule (for tuning; no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-layers", action="store_true", help="skip the per-layer records")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="only run --steps forwards of --layer (for rocprofv3)")
     ap.add_argument("--copy-probe", type=int, metavar="MIB",
                     help="only run a copy kernel of MIB MiB (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
-                    help="rocprofv3 --pmc output dirs (bench FETCH_SIZE, bench WRITE_SIZE, copy "
-                         "probe FETCH_SIZE, copy probe WRITE_SIZE): write profiles/traffic.json")
+                    help="rocprofv3 --pmc output dirs (FETCH_SIZE and WRITE_SIZE over --profile-run "
+                         "of --layer, then over the copy probe): record the layer in "
+                         "profiles/traffic.json")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
     if args.traffic_summary:
@@ -373,20 +505,22 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe, args.steps, dev)
         return
+    if args.profile_run:
+        profile_run(WL.LAYERS[args.layer], args.algo, args.steps, dev)
+        return
 
     if args.sweep:
         for name, L in WL.LAYERS.items():
             for algo in ("staged", "fused"):
                 r = run_layer(L, algo, args.steps, args.warmup, dev)
-                print(json.dumps({"layer": name, "algo": algo, "us": round(r["ms"] * 1e3, 2),
-                                  "TOPS": round(r["tops"], 2), "stages": r["stages"],
-                                  "direct_w8a8": r["direct"], "literal_input_stage": r["literal"]}),
-                      flush=True)
+                print(json.dumps({"layer": name, "algo": algo, **layer_entry(L, r)}), flush=True)
         return
 
     L = WL.LAYERS[args.layer]
-    r = run_layer(L, args.algo, args.steps, args.warmup, dev)
-    plan, dom = r["plan"], r["dom"]
+    r = run_layer(L, args.algo, args.steps, args.warmup, dev, extras=True)
+    plan = r["plan"]
+    dom = max(r["k_ms"], key=r["k_ms"].get)
+    st = r["stages"][dom]
     out = {
         "metric": "direct-conv-equiv int8 TOPS per layer, F(6,3); % MFMA int8 peak + HBM GB/s",
         "value": round(r["tops"], 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
@@ -395,21 +529,33 @@ def main():
         "config": {"workload": L.name, "m": L.m, "N": L.N, "Cin": L.Cin, "Cout": L.Cout,
                    "H": L.H, "W": L.W, "pad": L.pad, "group": L.G, "scales": L.scales,
                    "x_dtype": "f32", "tiles": plan.T,
-                   "schedule": "fused" if plan.fused else "staged"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(r["achieved"], 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+                   "schedule": "fused" if plan.fused else "staged",
+                   "timing": "K forwards captured in one HIP graph, replayed between two HIP events"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": st["GB_s"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": st["hbm_frac"],
+                     "cold_frac": st["cold_hbm_frac"],
                      "traffic": recorded_traffic(L.name, dom),
-                     "bytes_per_launch": r["nbytes"][dom]},
+                     "bytes_per_launch": r["nbytes"][dom], "avg_launch_us": st["us"]},
         "stages": r["stages"],
-        "baseline_direct_w8a8": r["direct"],
-        "literal_input_stage": r["literal"],
-        "accuracy": accuracy(L, r["d"], dev),
-        "per_step_ms": {"median": round(r["hot"][0], 5), "min": round(r["hot"][1], 5),
+        "per_step_ms": {"graph": round(r["ms"], 5), "eager": round(r["eager_ms"], 5),
                         "cold_median": round(r["cold"][0], 5), "cold_min": round(r["cold"][1], 5),
                         "cold_TOPS": round(L.direct_ops() / (r["cold"][0] * 1e-3) / 1e12, 3)},
-        "wall_s": round(r["wall"], 3),
+        "baseline_direct_w8a8": r["direct"],
+        "literal_input_stage": r["literal"],
+        "wall_s": round(r["wall"], 4),
     }
+    if "mfma" in st:
+        out["roofline"]["mfma"] = st["mfma"]
+    if not args.no_layers:
+        layers = {}
+        for name, Lx in WL.LAYERS.items():
+            if name == L.name:
+                layers[name] = layer_entry(L, r)
+                continue
+            layers[name] = layer_entry(Lx, run_layer(Lx, "auto", min(args.steps, 100),
+                                                     min(args.warmup, 10), dev))
+        out["layers"] = layers
+    out["accuracy"] = accuracy(L, r["d"], dev, images=min(L.N, 4 if L.N >= 32 else 2))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(L, r["d"])
         out["cpu_baseline"]["gpu_speedup_vs_oracle"] = round(out["value"] / out["cpu_baseline"]["value"], 1)

@@ -142,6 +142,13 @@ typedef struct {
     int fused_block;       /* fused block: 1 16 tiles x 16 output channels;
                               F(6,3) with G <= 64 also 2 32 x 32, 3 32 tiles x
                               16 channels, 4 16 tiles x 32 channels */
+    int stage2_rows;       /* staged Hadamard GEMM: 1 the LDS-pipelined kernel
+                              (64 tiles x 64 channels per block); 4, 5, 6 or 8
+                              the register-streamed kernel with that many
+                              16-tile rows per block */
+    int stage2_cols;       /* staged Hadamard GEMM: output channels per wave
+                              in units of 16: 1, or 2 for stage2_rows 4 or 5 */
+    int stage2_waves;      /* staged Hadamard GEMM: waves per block, 2 or 4 */
 } wq8_desc;
 
 /* Validates the descriptor and builds the scaled transforms on the host (exact

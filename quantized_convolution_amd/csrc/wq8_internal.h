@@ -36,6 +36,9 @@ struct Geo {
     int y_rows;               // 1: one Y scale per row of taps (staged only)
     int in_quant;             // wq8_inq: 0 fp32 input transform, 1/2 integer
     int s1_rows;              // stage-1 window: 0 chosen at launch, 1 all rows, 2 half the rows
+    int s2_rows;              // stage-2 block tiles / 16 (4, 5, 6, 8), 0 chosen at launch
+    int s2_cols;              // stage-2 channels per wave / 16 (1, 2), 0 chosen at launch
+    int s2_waves;             // stage-2 waves per block (2 or 4), 0 chosen at launch
 };
 
 // Nonzero patterns of B^T [n][n] and A^T [m][n] for the standard points
@@ -50,6 +53,10 @@ constexpr uint64_t kAtPattern6 = 0xfe7e7e7e7e7full;
 wq8_status fail(wq8_status st, const char *fmt, ...);
 void clear_error();
 
+// Compute units of the current HIP device (cached per device; 256 if the
+// query fails). Host code, for choosing launch shapes.
+int device_cus();
+
 // WQ8_OK, or WQ8_ERR_HIP with the pending launch error as detail.
 wq8_status check_launch(const char *what);
 
@@ -60,6 +67,8 @@ wq8_status launch_stage1(const Geo &g, const Mats &mt, wq8_dtype xdt, const void
                          int8_t *Vq, float *sV, void *stream);
 wq8_status launch_stage2(const Geo &g, const int8_t *Vq, const float *sV, const int8_t *Uq,
                          const float *sU, float *M, int32_t *P, void *stream);
+wq8_status launch_hgemm(const Geo &g, const int8_t *Vq, const float *sV, const int8_t *Uq,
+                        const float *sU, float *M, int32_t *P, void *stream);
 wq8_status launch_stage3(const Geo &g, const Mats &mt, wq8_dtype ydt, const float *M, void *y,
                          int8_t *Yq, float *sY, void *stream);
 wq8_status launch_fused23(const Geo &g, const Mats &mt, wq8_dtype ydt, const int8_t *Vq,

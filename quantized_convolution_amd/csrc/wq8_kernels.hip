@@ -1707,7 +1707,7 @@ wq8_status launch_weights(const Geo &g, const Mats &mt, const float *w, int8_t *
 }
 
 // Compute units of the current device (queried once per device).
-static int device_cus() {
+int device_cus() {
     static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
@@ -1824,6 +1824,12 @@ static void stage2_g(const Geo &g, const int8_t *Vq, const float *sV, const int8
 
 wq8_status launch_stage2(const Geo &g, const int8_t *Vq, const float *sV, const int8_t *Uq,
                          const float *sU, float *M, int32_t *P, void *stream) {
+    // Up to 128 input channels (one or two chunks) the LDS-pipelined kernel
+    // below is faster (ResNet-18 56 x 56 layer, staged: 14.6 against 20 us);
+    // from 256 channels on the register-streamed kernel (c5 layers: 70 -> 45
+    // us for 1280 channels, G = 32). stage2_rows forces one: 1 this kernel,
+    // 4, 5, 6 or 8 the other.
+    if (g.s2_rows > 1 || (g.s2_rows == 0 && g.Cin > 128)) return launch_hgemm(g, Vq, sV, Uq, sU, M, P, stream);
     hipStream_t s = (hipStream_t)stream;
     switch (g.G) {
         case 16: stage2_g<16>(g, Vq, sV, Uq, sU, M, P, s); break;

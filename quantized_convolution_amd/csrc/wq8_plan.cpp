@@ -501,6 +501,18 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
         return fail(WQ8_ERR_UNSUPPORTED, "wide fused blocks are built for F(6,3) with G <= 64 only");
     // Geo: -1 chosen at launch; 0 16 x 16; 1 32 x 32; 2 32 tiles x 16; 3 16 x 32
     p->geo.fused_wide = d->fused_block - 1;
+    if (d->stage2_rows != 0 && d->stage2_rows != 1 && d->stage2_rows != 4 && d->stage2_rows != 5 &&
+        d->stage2_rows != 6 && d->stage2_rows != 8)
+        return fail(WQ8_ERR_INVALID_ARG, "stage2_rows = %d: must be 0, 1, 4, 5, 6 or 8", d->stage2_rows);
+    p->geo.s2_rows = d->stage2_rows;
+    if (d->stage2_cols != 0 && d->stage2_cols != 1 && d->stage2_cols != 2)
+        return fail(WQ8_ERR_INVALID_ARG, "stage2_cols = %d: must be 0, 1 or 2", d->stage2_cols);
+    if (d->stage2_cols == 2 && (d->stage2_rows == 6 || d->stage2_rows == 8))
+        return fail(WQ8_ERR_UNSUPPORTED, "two channel tiles per wave are built for stage2_rows 4 and 5 only");
+    p->geo.s2_cols = d->stage2_cols;
+    if (d->stage2_waves != 0 && d->stage2_waves != 2 && d->stage2_waves != 4)
+        return fail(WQ8_ERR_INVALID_ARG, "stage2_waves = %d: must be 0, 2 or 4", d->stage2_waves);
+    p->geo.s2_waves = d->stage2_waves;
     return WQ8_OK;
 }
 

@@ -23,7 +23,9 @@ Neither is on the hot path; the library only consumes the scales.
 """
 from __future__ import annotations
 
+import json
 import math
+import os
 
 import numpy as np
 
@@ -198,3 +200,20 @@ def learn_scales(m: int, points=None, group: int = 64, steps: int = 200, lr: flo
     s_b = [float(np.float32(v)) for v in torch.exp(log_sb).detach().numpy()]
     s_g = [float(np.float32(v)) for v in torch.exp(log_sg).detach().numpy()]
     return s_b, s_g, hist
+
+
+# ------------------------------------------------------------ recorded sets
+LEARNED_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "data", "learned_scales.json")
+
+
+def recorded_learned_scales(m: int):
+    """(s_B, s_G) learned for F(m,3) by make_learned_scales.py, or None."""
+    try:
+        with open(LEARNED_FILE) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    e = rec.get(f"F({m},3)")
+    if e is None:
+        return None
+    return [float(v) for v in e["s_B"]], [float(v) for v in e["s_G"]]

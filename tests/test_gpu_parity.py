@@ -464,3 +464,38 @@ def test_per_row_y_scales(dev, name, kw):
     with pytest.raises(q.Wq8Error) as e:
         q.wq8_stage23(plan, *q.wq8_stage1(plan, to_dev(d["x"], dev)), Uq, sU)
     assert e.value.status == -2
+
+
+# every block shape of the register-streamed Hadamard kernel (stage2_rows
+# 4/5/6/8 x channel tiles 1/2 x 2/4 waves) and the LDS-pipelined one (1),
+# on layers with partial chunks (odd group counts), ragged tiles and
+# channels, and each group size
+HGEMM_SHAPES = [(1, 0, 0)] + [(r, c, w) for r in (4, 5, 6, 8) for c in (1, 2) for w in (2, 4)
+                              if not (c == 2 and r > 5)]
+HGEMM_LAYERS = [
+    WL.small(WL.LAYERS["c1_f4_n1_c16_16x16_g16"], N=2, H=15, W=13, Cin=80, Cout=37),     # G=16, 5 groups
+    WL.small(WL.LAYERS["c5_f6_n8_c640_32x32_g32"], N=1, H=29, W=31, Cin=160, Cout=70),   # G=32, 5 groups
+    WL.small(WL.LAYERS["c4_f6_n2_c320_64x64_g64_pert"], N=1, H=20, W=9, Cin=192, Cout=19),  # G=64, 3 groups
+    WL.small(WL.LAYERS["c5_f6_n8_c1280_16x16_g128"], N=2, H=11, W=16, Cin=384, Cout=33),  # G=128
+    WL.small(WL.LAYERS["c5_f6_n8_c1280_16x16_g128"], N=1, H=9, W=9, Cin=512, Cout=20).replace(G=256, name="h256"),
+]
+
+
+@pytest.mark.parametrize("L", HGEMM_LAYERS, ids=ids(HGEMM_LAYERS))
+def test_hgemm_block_shapes(dev, L):
+    """int32 partials and M bit-exact for every block shape of both Hadamard
+    kernels, from the oracle's codes."""
+    print(f"\n[case] hgemm shapes {L.name} G={L.G} Cin={L.Cin} Cout={L.Cout}", flush=True)
+    d = WL.make(L)
+    ref = oracle.forward(L.m, d["x"], d["w"], L.pad, L.G, points=list(d["points"]), s_b=d["s_b"],
+                         s_g=d["s_g"], keep=True)
+    P_ref = oracle.stage2_i32(ref["Vq"], ref["Uq"], L.G)
+    oVq, osV = to_dev(ref["Vq"], dev), to_dev(ref["sV"], dev)
+    oUq, osU = to_dev(ref["Uq"], dev), to_dev(ref["sU"], dev)
+    for rows, cols, waves in HGEMM_SHAPES:
+        plan = make_plan(L, d, algo="staged", stage2_rows=rows, stage2_cols=cols, stage2_waves=waves)
+        P = q.wq8_stage2_i32(plan, oVq, oUq)
+        M = q.wq8_stage2(plan, oVq, osV, oUq, osU)
+        torch.cuda.synchronize()
+        assert np.array_equal(P.cpu().numpy(), P_ref), f"P, shape {(rows, cols, waves)}"
+        assert np.array_equal(M.cpu().numpy(), ref["M"]), f"M, shape {(rows, cols, waves)}"
