@@ -39,19 +39,22 @@ from quantized_convolution_amd import workloads as WL  # noqa: E402
 HEADLINE = "c5_f6_n8_c1280_16x16_g32"  # the largest configuration (bytes moved per layer)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POP/s)
-KERNEL_SRC = os.path.join(ROOT, "quantized_convolution_amd", "csrc", "wq8_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "quantized_convolution_amd", "csrc", f)
+               for f in ("wq8_kernels.hip", "wq8_hgemm.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # name of each stage's kernel in a rocprofv3 trace (template prefix)
-KERNEL_NAMES = {"stage1": ("wq8::k_stage1<",), "stage2": ("wq8::k_stage2<",),
+KERNEL_NAMES = {"stage1": ("wq8::k_stage1<",), "stage2": ("wq8::k_stage2<", "wq8::k_hgemm<"),
                 "stage3": ("wq8::k_stage3<",),
                 "stage23": ("wq8::k_fused23<", "wq8::k_fused23w<")}
 
 
 def kernel_source_sha():
-    """Hash of the kernel source's code: comments and whitespace are dropped,
+    """Hash of the kernel sources' code: comments and whitespace are dropped,
     so only a change to the code itself marks recorded counters stale."""
-    with open(KERNEL_SRC, encoding="utf-8") as f:
-        src = f.read()
+    src = ""
+    for path in KERNEL_SRCS:
+        with open(path, encoding="utf-8") as f:
+            src += f.read() + "\n"
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     src = " ".join(src.split())

@@ -11,12 +11,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _sha_of(tmp_path, text):
     p = tmp_path / "k.hip"
     p.write_text(text)
-    old = bench.KERNEL_SRC
-    bench.KERNEL_SRC = str(p)
+    old = bench.KERNEL_SRCS
+    bench.KERNEL_SRCS = [str(p)]
     try:
         return bench.kernel_source_sha()
     finally:
-        bench.KERNEL_SRC = old
+        bench.KERNEL_SRCS = old
 
 
 def test_source_hash_ignores_comments_and_layout(tmp_path):
@@ -31,10 +31,10 @@ def test_recorded_traffic_follows_source_hash():
     # counters come back only while they were taken on the code as it stands
     rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
     current = rec["kernel_source_sha"] == bench.kernel_source_sha()
-    layer = "c2_f6_n32_c64_56x56_g64"
-    for kernel, v in rec["layers"][layer].items():
-        got = bench.recorded_traffic(layer, kernel)
-        assert got == (v["bytes_per_launch"] if current else None)
+    for layer in rec["layers"]:
+        for kernel, v in rec["layers"][layer].items():
+            got = bench.recorded_traffic(layer, kernel)
+            assert got == (v["bytes_per_launch"] if current else None)
     assert bench.recorded_traffic("no_such_layer", "stage1") is None
 
 
@@ -48,5 +48,6 @@ def test_stage_of_reads_the_template_arguments():
     assert bench.stage_of("void wq8::k_fused23<6, 64, 4, false, float>(a)") == "stage23"
     assert bench.stage_of("void wq8::k_fused23w<6, 64, false, float>(a)") == "stage23"
     assert bench.stage_of("void wq8::k_stage2<32, 64, false>(a)") == "stage2"
+    assert bench.stage_of("void wq8::k_hgemm<32, 5, 1, 4, false>(a)") == "stage2"
     assert bench.stage_of("void wq8::k_stage3<6, false, float>(a)") == "stage3"
     assert bench.stage_of("void wq8::k_weights<6, 64>(a)") is None
