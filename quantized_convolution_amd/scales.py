@@ -202,6 +202,59 @@ def learn_scales(m: int, points=None, group: int = 64, steps: int = 200, lr: flo
     return s_b, s_g, hist
 
 
+def learn_scales_model(m: int, layers, k: int = 3, steps: int = 300, lr: float = 0.02, seed: int = 0,
+                       init: str = "identity", noise: str = "gaussian", points=None):
+    """One shared (s_B, s_G) for a model's layers, learned without data: at
+    every step, k of the `layers` are drawn at random; each runs on fresh
+    noise inputs (zero-mean, unit variance: "gaussian" or "uniform") with
+    its own fixed weights; the loss is the mean over the k layers of the
+    negative output SQNR (dB) of the fake-quantized layer against the exact
+    convolution; Adam updates log s_B and log s_G, with straight-through
+    rounding. `layers` are dicts with w ([Cout][Cin][3][3] array), G, N, H,
+    W. Returns (s_B, s_G) as float32 lists and the loss history."""
+    import torch
+    import torch.nn.functional as F
+
+    points = list(standard_points(m) if points is None else points)
+    n = m + 2
+    if init == "equalizing":
+        b0, g0 = equalizing_scales(m, points)
+    elif init == "identity":
+        b0, g0 = [1.0] * n, [1.0] * n
+    else:
+        raise ValueError(init)
+    log_sb = torch.tensor(np.log(b0), dtype=torch.float64, requires_grad=True)
+    log_sg = torch.tensor(np.log(g0), dtype=torch.float64, requires_grad=True)
+    opt = torch.optim.Adam([log_sb, log_sg], lr=lr)
+    gen = torch.Generator().manual_seed(seed)
+    ws = [torch.as_tensor(np.asarray(L["w"], np.float64)) for L in layers]
+    hist = []
+    for _ in range(steps):
+        pick = torch.randperm(len(layers), generator=gen)[:k].tolist()
+        loss = 0.0
+        for i in pick:
+            L, w = layers[i], ws[i]
+            shape = (L["N"], w.shape[1], L["H"], L["W"])
+            if noise == "gaussian":
+                x = torch.randn(shape, generator=gen, dtype=torch.float64)
+            elif noise == "uniform":
+                x = (torch.rand(shape, generator=gen, dtype=torch.float64) * 2.0 - 1.0) * math.sqrt(3.0)
+            else:
+                raise ValueError(noise)
+            ref = F.conv2d(x, w, padding=1)
+            out = _layer_forward(m, points, log_sb, log_sg, x, w, L["G"])
+            err = torch.sum((out - ref) ** 2)
+            loss = loss - 10.0 * torch.log10(torch.sum(ref ** 2) / err)
+        loss = loss / len(pick)
+        opt.zero_grad()
+        loss.backward()
+        opt.step()
+        hist.append(float(loss.detach()))
+    s_b = [float(np.float32(v)) for v in torch.exp(log_sb).detach().numpy()]
+    s_g = [float(np.float32(v)) for v in torch.exp(log_sg).detach().numpy()]
+    return s_b, s_g, hist
+
+
 # ------------------------------------------------------------ recorded sets
 LEARNED_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "data", "learned_scales.json")
 

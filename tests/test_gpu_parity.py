@@ -225,6 +225,10 @@ def scale_set(L, which):
         return np.ones(n, np.float32), np.ones(n, np.float32)
     if which == "equalizing":
         return equalizing(L.m)
+    if which == "learned":
+        from quantized_convolution_amd import scales as S
+        sb, sg = S.recorded_learned_scales(L.m)
+        return np.array(sb, np.float32), np.array(sg, np.float32)
     raise ValueError(which)
 
 
@@ -293,11 +297,12 @@ def test_full_size_elementwise(dev, L):
           ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
 
 
-@pytest.mark.parametrize("which", ["standard", "equalizing"])
+@pytest.mark.parametrize("which", ["standard", "equalizing", "learned"])
 @pytest.mark.parametrize("L", FULL, ids=ids(FULL))
 def test_full_size_scale_sets(dev, L, which):
-    """Full configuration under the standard scales (S = I) and the
-    equalizing scales (F(6,3) s_B spans 0.13 to 24.8): codes and scales of
+    """Full configuration under the standard scales (S = I), the equalizing
+    scales (F(6,3) s_B spans 0.13 to 24.8) and the learned ones
+    (quantized_convolution_amd/data/learned_scales.json): codes and scales of
     every stage, and the forward the plan picks, element by element."""
     sb, sg = scale_set(L, which)
     print(f"\n[case] full {L.name} ({which} scales)", flush=True)

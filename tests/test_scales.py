@@ -97,3 +97,36 @@ def test_per_row_y_scales_do_not_rescue_standard_f63():
             out[yg, nm] = oracle.sqnr_db(ref, y)
     assert out["row", "I"] < 5.0 and out["tile", "I"] < 0.0
     assert out["row", "eq"] > out["row", "I"] + 10 and out["tile", "eq"] > out["tile", "I"] + 10
+
+
+@pytest.mark.parametrize("name", ["c2_f6_n32_c64_56x56_g64", "c4_f4_n2_c320_64x64_g64_pert",
+                                  "c5_f6_n8_c1280_16x16_g32"])
+def test_recorded_learned_scales_recover_the_layer(name):
+    """The shared scales learned on noise (data/learned_scales.json, written
+    by make_learned_scales.py) recover the layers the standard scales
+    collapse, to within 1 dB of the equalizing closed form, under the
+    oracle's quantized pipeline on the layer's own inputs (a few images and
+    channels of it)."""
+    L = WL.LAYERS[name]
+    L = WL.small(L, N=1, H=min(L.H, 20), W=min(L.W, 20), Cin=min(L.Cin, 2 * L.G if L.G >= 64 else 4 * L.G),
+                 Cout=16)
+    d = WL.make(L)
+    n = L.m + 2
+    learned = S.recorded_learned_scales(L.m)
+    assert learned is not None and len(learned[0]) == n and len(learned[1]) == n
+    got = {k: sqnr(L, d, *v) for k, v in {"standard": ([1.0] * n, [1.0] * n),
+                                          "equalizing": S.equalizing_scales(L.m),
+                                          "learned": learned}.items()}
+    print(got)
+    assert got["learned"] > got["standard"] + 10
+    assert got["learned"] >= got["equalizing"] - 1.0
+
+
+def test_learned_scales_record_the_procedure():
+    with open(S.LEARNED_FILE) as f:
+        rec = json.load(f)
+    st = rec["settings"]
+    assert st["noise"] in ("gaussian", "uniform") and st["k"] >= 1 and st["steps"] > 0
+    for m in (4, 6):
+        e = rec[f"F({m},3)"]
+        assert all(v > 0 for v in e["s_B"] + e["s_G"]) and e["loss_last10"] < e["loss_first"]
