@@ -898,7 +898,13 @@ __global__ __launch_bounds__(256) void k_stage2(const int8_t *__restrict__ Vq,
 // transform; otherwise one scale over all taps, applied to the result. The
 // m x m outputs go through LDS and leave as output rows: consecutive threads
 // write consecutive tiles of one row of one channel.
-template <int M, bool ROWS, typename YT>
+// Codes are rounded with x + 1.5 * 2^23 (exactly rint of the fp32 product,
+// which stays within +-127.5; the code is that sum minus 1.5 * 2^23, and its
+// low byte in two's complement). AMASK: the nonzero pattern of A^T when the
+// host has verified it (the standard points'); the chains skip the zero
+// terms, which is bit-identical (fma(0, y, acc) == acc: a chain starting at
+// +0 never holds -0).
+template <int M, bool ROWS, typename YT, uint64_t AMASK>
 __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT *__restrict__ y,
                                                 int8_t *__restrict__ Yq, float *__restrict__ sY,
                                                 Mats mt, Geo g) {
@@ -920,7 +926,7 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
 #pragma unroll
     for (int tap = 0; tap < NT; ++tap)
         mv[tap] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rM, moff, tap * (int)plane * 4, 0));
-    int q[NT];
+    float r[NT];  // x + 1.5 * 2^23 per tap (the code is r - 1.5 * 2^23)
     float yd[NT];
     float s = 1.0f;
 #pragma unroll
@@ -931,29 +937,27 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
         float a = 0.0f;
 #pragma unroll
         for (int k = 0; k < len; ++k) a = fmaxf(a, fabsf(mv[k0 + k]));
-        float sc = 0.0f, inv = 0.0f;
+        float sc = 0.0f, inv = 0.0f;  // a == 0: every code rounds to 0
         if (a != 0.0f) {
             inv = 127.0f / a;
             sc = a / 127.0f;
         }
 #pragma unroll
-        for (int k = 0; k < len; ++k) q[k0 + k] = a != 0.0f ? quant_code(mv[k0 + k], inv) : 0;
+        for (int k = 0; k < len; ++k) r[k0 + k] = mv[k0 + k] * inv + kRoundMagic;
         if (ok && sY) sY[ROWS ? idx * N + blk : idx] = sc;
         if constexpr (ROWS) {
 #pragma unroll
-            for (int k = 0; k < len; ++k) yd[k0 + k] = sc * (float)q[k0 + k];
+            for (int k = 0; k < len; ++k) yd[k0 + k] = sc * (r[k0 + k] - kRoundMagic);
         } else {
             s = sc;
 #pragma unroll
-            for (int k = 0; k < len; ++k) yd[k] = (float)q[k];
+            for (int k = 0; k < len; ++k) yd[k] = r[k] - kRoundMagic;
         }
     }
     if (ok && Yq) {
         uint32_t *yq = (uint32_t *)(Yq + idx * NT);  // NT is a multiple of 4
 #pragma unroll
-        for (int k = 0; k < NT; k += 4)
-            yq[k / 4] = (uint32_t)(q[k] & 255) | (uint32_t)(q[k + 1] & 255) << 8 |
-                        (uint32_t)(q[k + 2] & 255) << 16 | (uint32_t)(q[k + 3] & 255) << 24;
+        for (int k = 0; k < NT; k += 4) yq[k / 4] = pack4(r[k], r[k + 1], r[k + 2], r[k + 3]);
     }
 
     float z[M][N];
@@ -963,7 +967,8 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
         for (int j = 0; j < N; ++j) {
             float acc = 0.0f;
 #pragma unroll
-            for (int i = 0; i < N; ++i) acc = __builtin_fmaf(mt.At[aa * N + i], yd[i * N + j], acc);
+            for (int i = 0; i < N; ++i)
+                if ((AMASK >> (aa * N + i)) & 1) acc = __builtin_fmaf(mt.At[aa * N + i], yd[i * N + j], acc);
             z[aa][j] = acc;
         }
 #pragma unroll
@@ -972,7 +977,8 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
         for (int b = 0; b < M; ++b) {
             float acc = 0.0f;
 #pragma unroll
-            for (int j = 0; j < N; ++j) acc = __builtin_fmaf(z[aa][j], mt.At[b * N + j], acc);
+            for (int j = 0; j < N; ++j)
+                if ((AMASK >> (b * N + j)) & 1) acc = __builtin_fmaf(z[aa][j], mt.At[b * N + j], acc);
             s_out[ci][ti][aa * M + b] = ROWS ? acc : acc * s;
         }
     __syncthreads();
@@ -1845,8 +1851,16 @@ template <int M, typename YT>
 static void stage3_m(const Geo &g, const Mats &mt, const float *Mi, YT *y, int8_t *Yq, float *sY,
                      hipStream_t s) {
     dim3 grid((unsigned)((g.T + 7) / 8), (g.Cout + 31) / 32);
-    if (g.y_rows) hipLaunchKernelGGL((k_stage3<M, true, YT>), grid, dim3(256), 0, s, Mi, y, Yq, sY, mt, g);
-    else hipLaunchKernelGGL((k_stage3<M, false, YT>), grid, dim3(256), 0, s, Mi, y, Yq, sY, mt, g);
+    constexpr uint64_t pat = M == 4 ? kAtPattern4 : kAtPattern6;
+#define WQ8_S3(ROWS_, MASK_) hipLaunchKernelGGL((k_stage3<M, ROWS_, YT, MASK_>), grid, dim3(256), 0, s, Mi, y, Yq, sY, mt, g)
+    if (g.y_rows) {
+        if (g.at_std) WQ8_S3(true, pat);
+        else WQ8_S3(true, ~0ull);
+    } else {
+        if (g.at_std) WQ8_S3(false, pat);
+        else WQ8_S3(false, ~0ull);
+    }
+#undef WQ8_S3
 }
 
 // Fused block shape for a layer: waves per 16 x 16 block and the wide form
