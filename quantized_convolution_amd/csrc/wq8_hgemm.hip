@@ -359,15 +359,18 @@ __global__ __launch_bounds__(64 * NWV) void k_hgemm(const int8_t *__restrict__ V
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[ct][rt][i] = 0.0f;
 
-    // U ring: chunk c lives in slot c % DU from its load until its compute
+    // U ring: chunk c lives in slot c % DU from its load until its compute.
+    // Loads are issued without conditions, also for chunks past the last one
+    // (they read bytes that are never used, or zero past the buffer's end):
+    // with no branch between a load and its use the compiler waits for
+    // exactly the loads a step needs, not for every outstanding one.
     v4i ur[C::DU][C::CT][C::UP];
 #pragma unroll
-    for (int d = 0; d < C::DU; ++d)
-        if (d < nch) h2_issue_u<C>(ur[d], d, bs, rU);
+    for (int d = 0; d < C::DU; ++d) h2_issue_u<C>(ur[d], d, bs, rU);
     H2Stage<C> st;
     h2_issue_v<C, I32>(st, 0, bs, ps, g, rV, rsV, rsU);
     h2_commit_v<C, I32>(st, s_v[0], s_sv[0], s_su[0]);
-    if (nch > 1) h2_issue_v<C, I32>(st, 1, bs, ps, g, rV, rsV, rsU);
+    h2_issue_v<C, I32>(st, 1, bs, ps, g, rV, rsV, rsU);
     for (int c0 = 0; c0 < nch; c0 += C::DU) {
 #pragma unroll
         for (int d = 0; d < C::DU; ++d) {
@@ -375,13 +378,11 @@ __global__ __launch_bounds__(64 * NWV) void k_hgemm(const int8_t *__restrict__ V
             if (c >= nch) break;
             const int b = d & 1;  // c & 1, as DU is even and c0 a multiple of DU
             __syncthreads();      // chunk c is in buffer b; buffer b ^ 1 is free
-            if (c + 1 < nch) {
-                h2_commit_v<C, I32>(st, s_v[b ^ 1], s_sv[b ^ 1], s_su[b ^ 1]);
-                if (c + 2 < nch) h2_issue_v<C, I32>(st, c + 2, bs, ps, g, rV, rsV, rsU);
-            }
+            h2_commit_v<C, I32>(st, s_v[b ^ 1], s_sv[b ^ 1], s_su[b ^ 1]);
+            h2_issue_v<C, I32>(st, c + 2, bs, ps, g, rV, rsV, rsU);
             const int gin = min(C::GPC, g.ng - c * C::GPC);
             h2_chunk<C, I32>(acc, ur[d], c, gin, s_v[b], s_sv[b], s_su[b], ps, g, Po);
-            if (c + C::DU < nch) h2_issue_u<C>(ur[d], c + C::DU, bs, rU);
+            h2_issue_u<C>(ur[d], c + C::DU, bs, rU);
         }
     }
     if constexpr (!I32) {
