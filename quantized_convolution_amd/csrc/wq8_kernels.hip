@@ -32,26 +32,6 @@ __device__ __forceinline__ int quant_code(float v, float inv) {
     return (int)r;
 }
 
-// Max over aligned segments of SEG lanes (SEG a power of two <= 64).
-template <int SEG>
-__device__ __forceinline__ float seg_max(float a) {
-#pragma unroll
-    for (int s = 1; s < SEG; s <<= 1) a = fmaxf(a, __shfl_xor(a, s));
-    return a;
-}
-
-// --------------------------------------------------- per-channel transforms
-// Each lane owns one channel; a group of G channels spans SEG lanes of one
-// wave, or GW whole waves when G > 64. The block (256 threads) holds TPB
-// "rows" (tiles for stage 1, output channels for the weights).
-template <int G>
-struct GroupShape {
-    static constexpr int GW = G > 64 ? G / 64 : 1;   // waves per group
-    static constexpr int TPB = 4 / GW;               // rows per block
-    static constexpr int SEG = G < 64 ? G : 64;      // lanes reduced in-wave
-    static constexpr int CPB = 64 * GW;              // channels per block
-};
-
 // Quantize NT values per lane with per-tap group absmax and store codes and
 // scales. plane_codes/plane_scales are the per-tap strides.
 template <int NT, int G>
@@ -110,86 +90,6 @@ __device__ __forceinline__ void quantize_store(const float (&v)[NT], bool ok, in
 //      rounded with x + 1.5*2^23, whose low byte is rint(x) in two's
 //      complement (|x| <= 127 (1 + 2^-24)^2 < 127.5, so the clamp to +-127
 //      never binds and is omitted).
-
-// The group maxima are taken on bit patterns of |v|: non-negative floats
-// order like their unsigned bit patterns, so an integer max gives the float
-// max. (A float max of values that arrive through the integer cross-lane
-// moves would first have to quiet possible signalling NaNs, one more
-// instruction per operand.)
-
-// Reduce-scatter steps: pair a[i] with a[i + K/2]; each lane keeps one half
-// (the max over itself and its partner) and returns 1 if it kept the upper half.
-template <int K>
-__device__ __forceinline__ int rs_swap32(uint32_t (&a)[64]) {
-#pragma unroll
-    for (int i = 0; i < K / 2; ++i) {
-        auto r = __builtin_amdgcn_permlane32_swap(a[i], a[i + K / 2], false, false);
-        a[i] = max(r[0], r[1]);
-    }
-    auto lab = __builtin_amdgcn_permlane32_swap(0u, 1u, false, false);
-    return (int)lab[0];
-}
-
-template <int K>
-__device__ __forceinline__ int rs_swap16(uint32_t (&a)[64]) {
-#pragma unroll
-    for (int i = 0; i < K / 2; ++i) {
-        auto r = __builtin_amdgcn_permlane16_swap(a[i], a[i + K / 2], false, false);
-        a[i] = max(r[0], r[1]);
-    }
-    auto lab = __builtin_amdgcn_permlane16_swap(0u, 1u, false, false);
-    return (int)lab[0];
-}
-
-// DPP exchange with the lane given by CTRL; BIT is a lane-id bit that differs
-// between partners and decides which half a lane keeps.
-template <int K, int CTRL, int BIT>
-__device__ __forceinline__ int rs_dpp(uint32_t (&a)[64], int lane) {
-    const bool up = (lane >> BIT) & 1;
-#pragma unroll
-    for (int i = 0; i < K / 2; ++i) {
-        const uint32_t lo = a[i], hi = a[i + K / 2];
-        const uint32_t send = up ? lo : hi, keep = up ? hi : lo;
-        // old value 0 (the identity of the max) lets the move fold into the max
-        const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, CTRL, 0xf, 0xf, false);
-        a[i] = max(keep, recv);
-    }
-    return up;
-}
-
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kDppXor7 = 0x141;       // row_half_mirror: lane ^ 7 inside 8 lanes
-constexpr int kDppXor8 = 0x128;       // row_ror:8: lane ^ 8 inside 16 lanes
-
-// Max over SEG aligned lanes, for 64 values per lane (bit patterns of
-// non-negative floats). On return a[j], j < 64/SEG, holds the max for value
-// index base + j (base is returned).
-template <int SEG>
-__device__ __forceinline__ int reduce_scatter_max(uint32_t (&a)[64], int lane) {
-    int base = 0;
-    if constexpr (SEG == 64) {
-        base += rs_swap32<64>(a) * 32;
-        base += rs_swap16<32>(a) * 16;
-        base += rs_dpp<16, kDppXor8, 3>(a, lane) * 8;
-        base += rs_dpp<8, kDppXor7, 2>(a, lane) * 4;
-        base += rs_dpp<4, kDppXor2, 1>(a, lane) * 2;
-        base += rs_dpp<2, kDppXor1, 0>(a, lane);
-    } else if constexpr (SEG == 32) {
-        base += rs_swap16<64>(a) * 32;
-        base += rs_dpp<32, kDppXor8, 3>(a, lane) * 16;
-        base += rs_dpp<16, kDppXor7, 2>(a, lane) * 8;
-        base += rs_dpp<8, kDppXor2, 1>(a, lane) * 4;
-        base += rs_dpp<4, kDppXor1, 0>(a, lane) * 2;
-    } else {
-        static_assert(SEG == 16, "group lanes must be 16, 32 or 64");
-        base += rs_dpp<64, kDppXor8, 3>(a, lane) * 32;
-        base += rs_dpp<32, kDppXor7, 2>(a, lane) * 16;
-        base += rs_dpp<16, kDppXor2, 1>(a, lane) * 8;
-        base += rs_dpp<8, kDppXor1, 0>(a, lane) * 4;
-    }
-    return base;
-}
 
 // Stage 1 work item: a strip of TPB horizontally adjacent tiles of one tile
 // row, for CPB input channels. The strip's input window (CPB channels x n rows
@@ -342,7 +242,6 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW), RH ? 4 : 1) void k_s
     constexpr int N = M + 2, NT = N * N;
     using S = GroupShape<G>;
     using SS = S1Shape<M, G, TPB, RH>;
-    constexpr int KF = 64 / S::SEG;  // taps per lane after the reduce-scatter
     __shared__ float win[SS::CPB * SS::CS];
     __shared__ float red[S::GW > 1 ? SS::NW : 1][64];
     __shared__ __attribute__((aligned(16))) float inv_lds[SS::NW][64 / S::SEG][64];
@@ -351,7 +250,6 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW), RH ? 4 : 1) void k_s
     const int lane = threadIdx.x & 63;
     const int tl = wave / S::GW;                // this wave's tile in the strip
     const int cl = (wave % S::GW) * 64 + lane;  // this lane's channel in the block
-    const int seg = lane / S::SEG;
     const int n2 = N * N;
     const int plane = (int)g.T * g.Cin, splane = (int)g.T * g.ng;
     const auto rx = make_rsrc(x, (size_t)g.N * g.Cin * g.H * g.W * sizeof(XT));
@@ -497,64 +395,8 @@ __global__ __launch_bounds__((64 * S1Shape<M, G, TPB>::NW), RH ? 4 : 1) void k_s
                 }
         }
         }
-        // bit patterns of |v| (the reduction overwrites them; v is kept)
-        uint32_t a[64];
-        int base = 0;
-        if (!skip) {
-#pragma unroll
-            for (int i = 0; i < 64; ++i) a[i] = i < NT ? __float_as_uint(v[i]) & 0x7fffffffu : 0u;
-            base = reduce_scatter_max<S::SEG>(a, lane);
-        }
-        if constexpr (S::GW > 1) {
-            // the waves of one group share act, so they skip together
-            if (!skip)
-#pragma unroll
-                for (int j = 0; j < KF; ++j) red[wave][base + j] = __uint_as_float(a[j]);
-            __syncthreads();
-            const int w0 = (wave / S::GW) * S::GW;
-            if (!skip)
-#pragma unroll
-                for (int j = 0; j < KF; ++j) {
-                    float m = red[w0][base + j];
-#pragma unroll
-                    for (int k = 1; k < S::GW; ++k) m = fmaxf(m, red[w0 + k][base + j]);
-                    a[j] = __float_as_uint(m);
-                }
-        }
-        if (!skip)
-#pragma unroll
-        for (int j = 0; j < KF; ++j) {
-            const int tap = base + j;
-            const float am = __uint_as_float(a[j]);
-            float inv = 0.0f, sc = 0.0f;
-            if (am != 0.0f) {
-                inv = 127.0f / am;
-                sc = am / 127.0f;
-            }
-            inv_lds[wave][seg][tap] = inv;
-            if (ok && tap < NT && (S::GW == 1 || wave % S::GW == 0))
-                // tap differs between lanes, so it goes in the vector offset
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs,
-                                                      (tap * splane + t * g.ng + c / G) * 4, 0, 0);
-        }
-        __syncthreads();
-        if (ok) {
-            const int voff = t * g.Cin + c;
-#pragma unroll
-            for (int q4 = 0; q4 < (NT + 3) / 4; ++q4) {
-                const float4 iv = *(const float4 *)&inv_lds[wave][seg][4 * q4];
-                const float ivs[4] = {iv.x, iv.y, iv.z, iv.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int tap = 4 * q4 + e;
-                    if (tap < NT) {
-                        const float y = v[tap] * ivs[e] + kRoundMagic;
-                        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)__float_as_uint(y), rq, voff,
-                                                             tap * plane, 0);
-                    }
-                }
-            }
-        }
+        s1_quantize_store<NT, G, SS::NW>(v, skip, ok, wave, lane, c, t, g.Cin, g.ng, plane, splane, rq, rs,
+                                         red, inv_lds);
     }
 }
 
