@@ -375,16 +375,7 @@ def run_layer(L, algo, steps, warmup, dev, d=None, cold_reps=20, extras=False):
 
     # per-kernel durations: each stage entry point launches exactly the kernel
     # the forward launches, with the same grid
-    Vq = torch.empty(plan.vq_shape, dtype=torch.int8, device=dev)
-    sV = torch.empty(plan.sv_shape, dtype=torch.float32, device=dev)
-    q.wq8_stage1(plan, x, Vq, sV)
-    calls = {"stage1": lambda: q.wq8_stage1(plan, x, Vq, sV)}
-    if plan.fused:
-        calls["stage23"] = lambda: q.wq8_stage23(plan, Vq, sV, Uq, sU, y)
-    else:
-        M = torch.empty(plan.m_shape, dtype=torch.float32, device=dev)
-        calls["stage2"] = lambda: q.wq8_stage2(plan, Vq, sV, Uq, sU, M)
-        calls["stage3"] = lambda: q.wq8_stage3(plan, M, y)
+    calls = stage_calls(plan, x, Uq, sU, y, dev)
     iters = max(20, steps // 2)
     k_ms, k_cold = {}, {}
     for k, fn in calls.items():
@@ -415,6 +406,8 @@ def run_layer(L, algo, steps, warmup, dev, d=None, cold_reps=20, extras=False):
     # the literal input stage (quantized B^T and input patch, integer
     # transform): its stage-1 kernel and whole forward on the same workload
     lit = {}
+    Vq = torch.empty(plan.vq_shape, dtype=torch.int8, device=dev)
+    sV = torch.empty(plan.sv_shape, dtype=torch.float32, device=dev)
     for iq in ("int_tensor", "int_row"):
         pl = make_plan(L, d, algo, in_quant=iq)
         gs = capture(lambda: q.wq8_stage1(pl, x, Vq, sV), iters)
@@ -457,10 +450,29 @@ def layer_entry(L, r):
             "eager_forward_us": round(r["eager_ms"] * 1e3, 2), "stages": r["stages"]}
 
 
-def profile_run(L, algo, steps, dev):
-    """Only the forward of one layer, `steps` times (eager launches, one
-    process): the command rocprofv3 traces or counts for the summaries under
-    profiles/."""
+def stage_calls(plan, x, Uq, sU, y, dev):
+    """Each kernel of the forward through its stage entry point (the same
+    kernel and grid), on buffers of its own: the calls whose durations the
+    per-stage records and the roofline report."""
+    Vq = torch.empty(plan.vq_shape, dtype=torch.int8, device=dev)
+    sV = torch.empty(plan.sv_shape, dtype=torch.float32, device=dev)
+    q.wq8_stage1(plan, x, Vq, sV)
+    calls = {"stage1": lambda: q.wq8_stage1(plan, x, Vq, sV)}
+    if plan.fused:
+        calls["stage23"] = lambda: q.wq8_stage23(plan, Vq, sV, Uq, sU, y)
+    else:
+        M = torch.empty(plan.m_shape, dtype=torch.float32, device=dev)
+        calls["stage2"] = lambda: q.wq8_stage2(plan, Vq, sV, Uq, sU, M)
+        calls["stage3"] = lambda: q.wq8_stage3(plan, M, y)
+    return calls
+
+
+def profile_run(L, algo, steps, dev, stages=False):
+    """The command rocprofv3 traces or counts for the summaries under
+    profiles/ (one process): only the forward of one layer, `steps` times
+    (eager launches); or, with `stages`, each kernel as the per-stage timing
+    runs it (a HIP graph of `steps` back-to-back calls of its stage entry
+    point, replayed once, after one call outside the graph)."""
     d = WL.make(L)
     plan = make_plan(L, d, algo)
     x = torch.from_numpy(d["x"]).to(dev)
@@ -468,11 +480,18 @@ def profile_run(L, algo, steps, dev):
     y = plan.empty_output(dev)
     ws = plan.empty_workspace(dev)
     torch.cuda.synchronize()
-    for _ in range(steps):
-        q.wq8_conv_forward(plan, x, Uq, sU, y=y, workspace=ws)
+    if stages:
+        for fn in stage_calls(plan, x, Uq, sU, y, dev).values():
+            g = capture(fn, steps)
+            g.replay()
+            torch.cuda.synchronize()
+            del g
+    else:
+        for _ in range(steps):
+            q.wq8_conv_forward(plan, x, Uq, sU, y=y, workspace=ws)
     torch.cuda.synchronize()
     print(json.dumps({"profile_run": L.name, "schedule": "fused" if plan.fused else "staged",
-                      "forwards": steps}), flush=True)
+                      "what": "stage graphs" if stages else "forwards", "calls": steps}), flush=True)
 
 
 def main():
@@ -488,6 +507,9 @@ def main():
     ap.add_argument("--no-layers", action="store_true", help="skip the per-layer records")
     ap.add_argument("--profile-run", action="store_true",
                     help="only run --steps forwards of --layer (for rocprofv3)")
+    ap.add_argument("--profile-stages", action="store_true",
+                    help="with --profile-run: each kernel as the per-stage timing runs it (a graph of "
+                         "--steps calls of its stage entry point)")
     ap.add_argument("--copy-probe", type=int, metavar="MIB",
                     help="only run a copy kernel of MIB MiB (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
@@ -509,7 +531,7 @@ def main():
         copy_probe(args.copy_probe, args.steps, dev)
         return
     if args.profile_run:
-        profile_run(WL.LAYERS[args.layer], args.algo, args.steps, dev)
+        profile_run(WL.LAYERS[args.layer], args.algo, args.steps, dev, stages=args.profile_stages)
         return
 
     if args.sweep:

@@ -132,16 +132,18 @@ __device__ __forceinline__ void h2_bases(H2Base<C> &bs, const H2Pos &ps, const G
 
 // Issue the loads of chunk c of V and of the chunk's group scales. A chunk
 // that ends past a row's last group reads the next row's bytes (or zero past
-// the buffer) into group slots that are never computed.
+// the buffer) into group slots that are never computed. For a chunk past the
+// last one (c >= nch) the offsets are out of range: the loads return zero
+// and fetch nothing.
 template <class C, bool I32>
-__device__ __forceinline__ void h2_issue_v(H2Stage<C> &st, int c, const H2Base<C> &bs, const H2Pos &ps,
-                                           const Geo &g, __amdgpu_buffer_rsrc_t rV,
+__device__ __forceinline__ void h2_issue_v(H2Stage<C> &st, int c, int nch, const H2Base<C> &bs,
+                                           const H2Pos &ps, const Geo &g, __amdgpu_buffer_rsrc_t rV,
                                            __amdgpu_buffer_rsrc_t rsV, __amdgpu_buffer_rsrc_t rsU) {
-    const uint32_t cb = (uint32_t)(c * C::KC);
+    const uint32_t cb = c < nch ? (uint32_t)(c * C::KC) : (uint32_t)kOob;
 #pragma unroll
     for (int j = 0; j < C::LPV; ++j) st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rV, (int)(bs.v[j] + cb), 0, 0);
     if constexpr (!I32) {
-        const uint32_t sb = (uint32_t)(c * C::GPC * 4);
+        const uint32_t sb = c < nch ? (uint32_t)(c * C::GPC * 4) : (uint32_t)kOob;
 #pragma unroll
         for (int j = 0; j < C::SPV; ++j)
             st.sv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsV, (int)(bs.sv[j] + sb), 0, 0));
@@ -187,11 +189,12 @@ __device__ __forceinline__ void h2_commit_v(const H2Stage<C> &st, int8_t *op, fl
     }
 }
 
-// Issue the U loads of chunk c into one ring slot.
+// Issue the U loads of chunk c into one ring slot (out of range, so zero and
+// no fetch, for a chunk past the last one).
 template <class C>
-__device__ __forceinline__ void h2_issue_u(v4i (&u)[C::CT][C::UP], int c, const H2Base<C> &bs,
+__device__ __forceinline__ void h2_issue_u(v4i (&u)[C::CT][C::UP], int c, int nch, const H2Base<C> &bs,
                                            __amdgpu_buffer_rsrc_t rU) {
-    const uint32_t cb = (uint32_t)(c * C::KC);
+    const uint32_t cb = c < nch ? (uint32_t)(c * C::KC) : (uint32_t)kOob;
 #pragma unroll
     for (int ct = 0; ct < C::CT; ++ct) {
         if constexpr (C::G == 16) {
@@ -361,16 +364,16 @@ __global__ __launch_bounds__(64 * NWV) void k_hgemm(const int8_t *__restrict__ V
 
     // U ring: chunk c lives in slot c % DU from its load until its compute.
     // Loads are issued without conditions, also for chunks past the last one
-    // (they read bytes that are never used, or zero past the buffer's end):
+    // (with out-of-range offsets, chosen by a select, so they fetch nothing):
     // with no branch between a load and its use the compiler waits for
     // exactly the loads a step needs, not for every outstanding one.
     v4i ur[C::DU][C::CT][C::UP];
 #pragma unroll
-    for (int d = 0; d < C::DU; ++d) h2_issue_u<C>(ur[d], d, bs, rU);
+    for (int d = 0; d < C::DU; ++d) h2_issue_u<C>(ur[d], d, nch, bs, rU);
     H2Stage<C> st;
-    h2_issue_v<C, I32>(st, 0, bs, ps, g, rV, rsV, rsU);
+    h2_issue_v<C, I32>(st, 0, nch, bs, ps, g, rV, rsV, rsU);
     h2_commit_v<C, I32>(st, s_v[0], s_sv[0], s_su[0]);
-    h2_issue_v<C, I32>(st, 1, bs, ps, g, rV, rsV, rsU);
+    h2_issue_v<C, I32>(st, 1, nch, bs, ps, g, rV, rsV, rsU);
     for (int c0 = 0; c0 < nch; c0 += C::DU) {
 #pragma unroll
         for (int d = 0; d < C::DU; ++d) {
@@ -379,10 +382,10 @@ __global__ __launch_bounds__(64 * NWV) void k_hgemm(const int8_t *__restrict__ V
             const int b = d & 1;  // c & 1, as DU is even and c0 a multiple of DU
             __syncthreads();      // chunk c is in buffer b; buffer b ^ 1 is free
             h2_commit_v<C, I32>(st, s_v[b ^ 1], s_sv[b ^ 1], s_su[b ^ 1]);
-            h2_issue_v<C, I32>(st, c + 2, bs, ps, g, rV, rsV, rsU);
+            h2_issue_v<C, I32>(st, c + 2, nch, bs, ps, g, rV, rsV, rsU);
             const int gin = min(C::GPC, g.ng - c * C::GPC);
             h2_chunk<C, I32>(acc, ur[d], c, gin, s_v[b], s_sv[b], s_su[b], ps, g, Po);
-            h2_issue_u<C>(ur[d], c + C::DU, bs, rU);
+            h2_issue_u<C>(ur[d], c + C::DU, nch, bs, rU);
         }
     }
     if constexpr (!I32) {
