@@ -65,7 +65,12 @@ struct H2 {
     // U registers per lane per chunk and channel tile, in 16-byte pieces
     // (G = 16: each piece holds two 8-byte group slices)
     static constexpr int UP = G == 16 ? KC / 32 : KC / 64;
-    static constexpr int DU = 2;                         // U chunks in flight per wave
+    // U chunks in flight per wave: 4 for the shapes that still fit in 128
+    // registers with them (four waves per SIMD; the deeper ring hides more of
+    // HBM's latency when the weights are not cached: 5 % on the 1280-channel
+    // layer), else 2 (more registers would cost a wave per SIMD, which costs
+    // more than the ring gains)
+    static constexpr int DU = RT <= 5 && CT == 1 && NWV == 4 && G >= 32 && G <= 128 ? 4 : 2;
 };
 
 struct H2Pos {
