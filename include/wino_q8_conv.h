@@ -149,6 +149,8 @@ typedef struct {
     int stage2_cols;       /* staged Hadamard GEMM: output channels per wave
                               in units of 16: 1, or 2 for stage2_rows 4 or 5 */
     int stage2_waves;      /* staged Hadamard GEMM: waves per block, 2 or 4 */
+    int stage3_lanes;      /* staged output transform: lanes per (tile, output
+                              channel) pair, 1 or 2 */
 } wq8_desc;
 
 /* Validates the descriptor and builds the scaled transforms on the host (exact

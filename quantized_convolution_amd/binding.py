@@ -38,7 +38,7 @@ class wq8_desc(C.Structure):
                 ("x_dtype", C.c_int), ("y_dtype", C.c_int), ("algo", C.c_int), ("y_group", C.c_int),
                 ("in_quant", C.c_int), ("stage1_rows", C.c_int), ("fused_waves", C.c_int),
                 ("fused_block", C.c_int), ("stage2_rows", C.c_int), ("stage2_cols", C.c_int),
-                ("stage2_waves", C.c_int)]
+                ("stage2_waves", C.c_int), ("stage3_lanes", C.c_int)]
 
 
 EXPORTS = ("wq8_plan_create", "wq8_plan_destroy", "wq8_plan_query", "wq8_plan_matrices",
@@ -156,13 +156,14 @@ class Plan:
     def __init__(self, m, N, Cin, Cout, H, W, pad=1, group=64, points=None, s_B=None, s_G=None,
                  x_dtype=torch.float32, y_dtype=None, algo="auto", y_group="tile",
                  in_quant="fp32", stage1_rows=0, fused_waves=0, fused_block=0, stage2_rows=0,
-                 stage2_cols=0, stage2_waves=0):
+                 stage2_cols=0, stage2_waves=0, stage3_lanes=0):
         """Kernel shapes (0 = the library chooses; results never depend on
         them): stage1_rows 1 all / 2 half the input rows in the LDS window;
         fused_waves 4, 8 or 16; fused_block 1 16x16, 2 32x32, 3 32 tiles x 16
         channels, 4 16 x 32; stage2_rows 4, 5, 6 or 8 (tiles per staged
         Hadamard block / 16); stage2_cols 1 or 2 (channels per wave / 16);
-        stage2_waves 2 or 4."""
+        stage2_waves 2 or 4; stage3_lanes 1 or 2 (lanes per (tile, channel) pair
+        of the staged output transform)."""
         lib = load()
         n = m + 2
         self.m, self.n, self.N, self.Cin, self.Cout, self.H, self.W = m, n, N, Cin, Cout, H, W
@@ -186,7 +187,7 @@ class Plan:
                      arr(s_G, C.c_float, np.float32), group, N, Cin, Cout, H, W, pad,
                      _DT[self.x_dtype], _DT[self.y_dtype], ALGOS[algo], YGROUPS[y_group],
                      IN_QUANTS[in_quant], int(stage1_rows), int(fused_waves), int(fused_block),
-                     int(stage2_rows), int(stage2_cols), int(stage2_waves))
+                     int(stage2_rows), int(stage2_cols), int(stage2_waves), int(stage3_lanes))
         h = C.c_void_p()
         self._h = None
         _check(wq8_plan_create(d, h))

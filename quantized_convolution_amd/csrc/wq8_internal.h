@@ -39,6 +39,7 @@ struct Geo {
     int s2_rows;              // stage-2 block tiles / 16 (4, 5, 6, 8), 0 chosen at launch
     int s2_cols;              // stage-2 channels per wave / 16 (1, 2), 0 chosen at launch
     int s2_waves;             // stage-2 waves per block (2 or 4), 0 chosen at launch
+    int s3_lanes;             // stage-3 lanes per (tile, co) pair (1 or 2), 0 chosen at launch
 };
 
 // Nonzero patterns of B^T [n][n] and A^T [m][n] for the standard points

@@ -746,6 +746,42 @@ __global__ __launch_bounds__(256) void k_stage2(const int8_t *__restrict__ Vq,
 // host has verified it (the standard points'); the chains skip the zero
 // terms, which is bit-identical (fma(0, y, acc) == acc: a chain starting at
 // +0 never holds -0).
+// Stage-3 outputs of a block of NTH threads (TI tiles x CI output channels,
+// m x m pixels each, in LDS as s_out[ci][ti][pixel]) to y, one output row of
+// one tile per thread step, consecutive threads on consecutive tiles. (Left
+// rolled: unrolling this loop made stage 3 5-8 % slower.)
+template <int M, int CI, int TI, int NTH, typename YT>
+__device__ __forceinline__ void s3_store(const float (*s_out)[TI][M * M + 1], int t0, int c0, YT *y,
+                                         const Geo &g) {
+    for (int e = threadIdx.x; e < CI * TI * M; e += NTH) {
+        const int eti = e % TI, rest = e / TI;
+        const int aa = rest % M, eci = rest / M;
+        const int et = t0 + eti, eco = c0 + eci;
+        if (et >= g.T || eco >= g.Cout) continue;
+        const int tx = et % g.tW, rr = et / g.tW, ty = rr % g.tH, img = rr / g.tH;
+        const int h = ty * M + aa;
+        if (h >= g.Ho) continue;
+        YT *yp = y + (((size_t)img * g.Cout + eco) * g.Ho + h) * g.Wo + (size_t)tx * M;
+        const int nb = min(M, g.Wo - tx * M);
+        if constexpr (M % 2 == 0) {
+            // with m and Wo even a tile's row starts at an even element, so
+            // pairs of pixels go out as one store (8 bytes fp32, 4 bytes bf16)
+            if (g.Wo % 2 == 0) {
+#pragma unroll
+                for (int b = 0; b < M; b += 2) {
+                    const float v0 = s_out[eci][eti][aa * M + b], v1 = s_out[eci][eti][aa * M + b + 1];
+                    if (b + 1 < nb) store_act2(yp + b, v0, v1);
+                    else if (b < nb) store_act(yp + b, v0);
+                }
+                continue;
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < M; ++b)
+            if (b < nb) store_act(yp + b, s_out[eci][eti][aa * M + b]);
+    }
+}
+
 template <int M, bool ROWS, typename YT, uint64_t AMASK>
 __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT *__restrict__ y,
                                                 int8_t *__restrict__ Yq, float *__restrict__ sY,
@@ -824,34 +860,133 @@ __global__ __launch_bounds__(256) void k_stage3(const float *__restrict__ Mi, YT
             s_out[ci][ti][aa * M + b] = ROWS ? acc : acc * s;
         }
     __syncthreads();
-    // rows (ci, ti, aa): CI * TI * M of them, consecutive threads on consecutive tiles
-    for (int e = tid; e < CI * TI * M; e += 256) {
-        const int eti = e % TI, rest = e / TI;
-        const int aa = rest % M, eci = rest / M;
-        const int et = t0 + eti, eco = c0 + eci;
-        if (et >= g.T || eco >= g.Cout) continue;
-        const int tx = et % g.tW, rr = et / g.tW, ty = rr % g.tH, img = rr / g.tH;
-        const int h = ty * M + aa;
-        if (h >= g.Ho) continue;
-        YT *yp = y + (((size_t)img * g.Cout + eco) * g.Ho + h) * g.Wo + (size_t)tx * M;
-        const int nb = min(M, g.Wo - tx * M);
-        if constexpr (M % 2 == 0) {
-            // with m and Wo even a tile's row starts at an even element, so
-            // pairs of pixels go out as one store (8 bytes fp32, 4 bytes bf16)
-            if (g.Wo % 2 == 0) {
+    s3_store<M, CI, TI, 256>(s_out, t0, c0, y, g);
+}
+
+// Stage 3 with two lanes per (tile, co) pair, for layers with few pairs
+// (one lane per pair would leave the SIMDs one or two waves each). Lane l
+// (half h = l / 32) and lane l + 32 share a pair; lane h holds the taps of
+// columns [h n/2, (h+1) n/2) of all n rows. The Y absmax (of the pair, or of
+// each row of taps) meets across the halves through one permlane32 swap; the
+// first pass z = A^T Yq runs over rows in index order inside each lane (its
+// columns); then a permlane32 swap per (row of z, column) gives lane h rows
+// [h m/2, (h+1) m/2) of z with all n columns, in column order, and the second
+// pass O = z A over columns in index order produces those output rows. Every
+// chain is the one-lane kernel's chain, so codes, scales and outputs are
+// bit-identical to it.
+template <int M, bool ROWS, typename YT, uint64_t AMASK>
+__global__ __launch_bounds__(256) void k_stage3h(const float *__restrict__ Mi, YT *__restrict__ y,
+                                                 int8_t *__restrict__ Yq, float *__restrict__ sY,
+                                                 Mats mt, Geo g) {
+    constexpr int N = M + 2, NT = N * N, MM = M * M;
+    constexpr int NH = N / 2, MH = M / 2;  // columns and output rows per lane
+    constexpr int TI = 4, CI = 32;         // one tile per wave, 32 channels per half
+    __shared__ float s_out[CI][TI][MM + 1];
+    const int lane = threadIdx.x & 63, h = lane >> 5, ci = lane & 31;
+    const int ti = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * TI, c0 = blockIdx.y * CI;
+    const int t = t0 + ti, co = c0 + ci;
+    const bool ok = t < g.T && co < g.Cout;
+    const int plane = (int)g.T * g.Cout;  // n^2 * plane * 4 (M's bytes) is below 2^31
+    const int idx = t * g.Cout + co;
+    const auto rM = make_rsrc(Mi, (size_t)NT * plane * 4);
+    // tap (i, h NH + jj) at byte idx * 4 + tap * plane * 4; the lane's column
+    // offset goes in the vector offset, the tap's row and column in the
+    // scalar one (out of range for pairs outside the layer)
+    const int moff = ok ? (idx + h * NH * plane) * 4 : kOob;
+    float mv[N][NH];
 #pragma unroll
-                for (int b = 0; b < M; b += 2) {
-                    const float v0 = s_out[eci][eti][aa * M + b], v1 = s_out[eci][eti][aa * M + b + 1];
-                    if (b + 1 < nb) store_act2(yp + b, v0, v1);
-                    else if (b < nb) store_act(yp + b, v0);
-                }
-                continue;
-            }
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NH; ++jj)
+            mv[i][jj] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rM, moff, (i * N + jj) * plane * 4, 0));
+    // max of the two halves' non-negative maxima, on bit patterns
+    auto pair_max = [](float a) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+        return __uint_as_float(max(r[0], r[1]));
+    };
+    float r[N][NH];   // x + 1.5 * 2^23 per tap (the code is r - 1.5 * 2^23)
+    float yd[N][NH];
+    float s = 1.0f;
+#pragma unroll
+    for (int blk = 0; blk < (ROWS ? N : 1); ++blk) {
+        constexpr int rows = ROWS ? 1 : N;  // rows of taps under one scale
+        const int i0 = blk * rows;
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < rows; ++i)
+#pragma unroll
+            for (int jj = 0; jj < NH; ++jj) a = fmaxf(a, fabsf(mv[i0 + i][jj]));
+        a = pair_max(a);
+        float sc = 0.0f, inv = 0.0f;  // a == 0: every code rounds to 0
+        if (a != 0.0f) {
+            inv = 127.0f / a;
+            sc = a / 127.0f;
         }
 #pragma unroll
-        for (int b = 0; b < M; ++b)
-            if (b < nb) store_act(yp + b, s_out[eci][eti][aa * M + b]);
+        for (int i = 0; i < rows; ++i)
+#pragma unroll
+            for (int jj = 0; jj < NH; ++jj) r[i0 + i][jj] = mv[i0 + i][jj] * inv + kRoundMagic;
+        if (ok && sY && h == 0) sY[ROWS ? (size_t)idx * N + blk : (size_t)idx] = sc;
+        if constexpr (ROWS) {
+#pragma unroll
+            for (int jj = 0; jj < NH; ++jj) yd[blk][jj] = sc * (r[blk][jj] - kRoundMagic);
+        } else {
+            s = sc;
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+#pragma unroll
+                for (int jj = 0; jj < NH; ++jj) yd[i][jj] = r[i][jj] - kRoundMagic;
+        }
     }
+    if (ok && Yq) {
+        int8_t *yq = Yq + (size_t)idx * NT + h * NH;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            if constexpr (NH == 4)
+                *(uint32_t *)(yq + i * N) = pack4(r[i][0], r[i][1], r[i][2], r[i][3]);
+            else
+#pragma unroll
+                for (int jj = 0; jj < NH; ++jj) yq[i * N + jj] = (int8_t)__float_as_uint(r[i][jj]);
+        }
+    }
+    // first pass on this lane's columns: z[aa][jj] = sum_i A^T[aa][i] yd[i][jj]
+    float z[M][NH];
+#pragma unroll
+    for (int aa = 0; aa < M; ++aa)
+#pragma unroll
+        for (int jj = 0; jj < NH; ++jj) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                if ((AMASK >> (aa * N + i)) & 1) acc = __builtin_fmaf(mt.At[aa * N + i], yd[i][jj], acc);
+            z[aa][jj] = acc;
+        }
+    // swap(x = z[rr], y = z[MH + rr]): the lower half gets row rr (its own
+    // columns in r0, the upper half's in r1), the upper half row MH + rr (the
+    // lower half's columns in r0, its own in r1)
+    float zr[MH][N];
+#pragma unroll
+    for (int rr = 0; rr < MH; ++rr)
+#pragma unroll
+        for (int jj = 0; jj < NH; ++jj) {
+            const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(z[rr][jj]), __float_as_uint(z[MH + rr][jj]),
+                                                            false, false);
+            zr[rr][jj] = __uint_as_float(w[0]);
+            zr[rr][NH + jj] = __uint_as_float(w[1]);
+        }
+#pragma unroll
+    for (int rr = 0; rr < MH; ++rr)
+#pragma unroll
+        for (int b = 0; b < M; ++b) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < N; ++j)
+                if ((AMASK >> (b * N + j)) & 1) acc = __builtin_fmaf(zr[rr][j], mt.At[b * N + j], acc);
+            s_out[ci][ti][(h * MH + rr) * M + b] = ROWS ? acc : acc * s;
+        }
+    __syncthreads();
+    s3_store<M, CI, TI, 256>(s_out, t0, c0, y, g);
 }
 
 // ------------------------------------------------- fused stages 2 + 3
@@ -1689,11 +1824,36 @@ wq8_status launch_stage2(const Geo &g, const int8_t *Vq, const float *sV, const 
     return check_launch("Hadamard GEMM");
 }
 
+// Two lanes per (tile, co) pair when one lane per pair gives the device
+// fewer than 1.25 waves per SIMD (the plan's stage3_lanes may force 1 or 2).
+// Measured stage 3 (one lane -> two): 7 x 7, C = 512 (1.0 waves per SIMD)
+// 6.8 -> 5.6 us; 14 x 14, C = 256 (1.1) 8.7 -> 7.9 us; 16 x 16, C = 1280
+// (1.4) 10.0 either way; 64 x 64, C = 320, F(4,3) (2.5) 6.9 -> 7.3 us;
+// 32 x 32, C = 640 (2.8) 15.3 -> 17.6 us.
+static bool stage3_split(const Geo &g, int cus) {
+    if (g.s3_lanes) return g.s3_lanes == 2;
+    const int64_t waves = (g.T * (int64_t)g.Cout + 63) / 64;
+    return 4 * waves < 5 * 4 * (int64_t)cus;
+}
+
 template <int M, typename YT>
 static void stage3_m(const Geo &g, const Mats &mt, const float *Mi, YT *y, int8_t *Yq, float *sY,
                      hipStream_t s) {
-    dim3 grid((unsigned)((g.T + 7) / 8), (g.Cout + 31) / 32);
     constexpr uint64_t pat = M == 4 ? kAtPattern4 : kAtPattern6;
+    if (stage3_split(g, device_cus())) {
+        dim3 grid((unsigned)((g.T + 3) / 4), (g.Cout + 31) / 32);
+#define WQ8_S3(ROWS_, MASK_) hipLaunchKernelGGL((k_stage3h<M, ROWS_, YT, MASK_>), grid, dim3(256), 0, s, Mi, y, Yq, sY, mt, g)
+        if (g.y_rows) {
+            if (g.at_std) WQ8_S3(true, pat);
+            else WQ8_S3(true, ~0ull);
+        } else {
+            if (g.at_std) WQ8_S3(false, pat);
+            else WQ8_S3(false, ~0ull);
+        }
+#undef WQ8_S3
+        return;
+    }
+    dim3 grid((unsigned)((g.T + 7) / 8), (g.Cout + 31) / 32);
 #define WQ8_S3(ROWS_, MASK_) hipLaunchKernelGGL((k_stage3<M, ROWS_, YT, MASK_>), grid, dim3(256), 0, s, Mi, y, Yq, sY, mt, g)
     if (g.y_rows) {
         if (g.at_std) WQ8_S3(true, pat);

@@ -513,6 +513,9 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
     if (d->stage2_waves != 0 && d->stage2_waves != 2 && d->stage2_waves != 4)
         return fail(WQ8_ERR_INVALID_ARG, "stage2_waves = %d: must be 0, 2 or 4", d->stage2_waves);
     p->geo.s2_waves = d->stage2_waves;
+    if (d->stage3_lanes < 0 || d->stage3_lanes > 2)
+        return fail(WQ8_ERR_INVALID_ARG, "stage3_lanes = %d: must be 0, 1 or 2", d->stage3_lanes);
+    p->geo.s3_lanes = d->stage3_lanes;
     return WQ8_OK;
 }
 

@@ -471,6 +471,40 @@ def test_per_row_y_scales(dev, name, kw):
     assert e.value.status == -2
 
 
+@pytest.mark.parametrize("y_group", ["tile", "row"])
+@pytest.mark.parametrize("name,kw,ydt", [
+    ("c5_f6_n8_c1280_16x16_g32", dict(N=2, H=16, W=16, Cin=64, Cout=50), torch.float32),   # 18 tiles
+    ("c4_f4_n2_c320_64x64_g64_pert", dict(N=1, H=13, W=22, Cin=64, Cout=33), torch.float32),
+    ("c5_f6_n8_c640_32x32_g128", dict(N=1, H=20, W=14, Cin=128, Cout=40), torch.bfloat16),
+    ("c3c_f6_n32_c512_7x7_g64", dict(N=3, H=7, W=7, Cin=64, Cout=70), torch.float32),       # odd W, 12 tiles
+])
+def test_stage3_lanes(dev, name, kw, ydt, y_group):
+    """The output transform with one lane per (tile, channel) pair and with
+    two (each holding half the columns of taps; the launch takes two on
+    layers with few pairs; stage3_lanes forces either): Y codes and scales
+    bit-exact from the oracle's M for both, and the two outputs bit-identical
+    (the same fma chains), within tolerance of the oracle."""
+    L = WL.small(WL.LAYERS[name], **kw)
+    print(f"\n[case] stage-3 lanes {L.name} {ydt} y_group={y_group}", flush=True)
+    d = WL.make(L)
+    ref = oracle.forward(L.m, d["x"], d["w"], L.pad, L.G, points=list(d["points"]), s_b=d["s_b"],
+                         s_g=d["s_g"], keep=True, y_group=y_group)
+    M = to_dev(ref["M"], dev)
+    outs = {}
+    for lanes in (1, 2):
+        plan = q.Plan(L.m, L.N, L.Cin, L.Cout, L.H, L.W, L.pad, L.G, points=d["points"], s_B=d["s_b"],
+                      s_G=d["s_g"], y_dtype=ydt, algo="staged", y_group=y_group, stage3_lanes=lanes)
+        y3, Yq, sY = q.wq8_stage3(plan, M, want_codes=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(Yq.cpu().numpy(), ref["Yq"]), f"Yq, {lanes} lane(s)"
+        assert np.array_equal(sY.cpu().numpy(), ref["sY"]), f"sY, {lanes} lane(s)"
+        outs[lanes] = y3.cpu()
+    assert torch.equal(outs[1].view(torch.int16 if ydt == torch.bfloat16 else torch.int32),
+                       outs[2].view(torch.int16 if ydt == torch.bfloat16 else torch.int32))
+    if ydt == torch.float32:
+        assert_out(outs[2].numpy(), ref["y"], "stage-3 output")
+
+
 # every block shape of the register-streamed Hadamard kernel (stage2_rows
 # 4/5/6/8 x channel tiles 1/2 x 2/4 waves) and the LDS-pipelined one (1),
 # on layers with partial chunks (odd group counts), ragged tiles and

@@ -41,7 +41,7 @@ def _create(**kw):
     base = dict(m=6, points=None, s_B=None, s_G=None, group=64, N=1, Cin=64, Cout=64, H=16, W=16,
                 pad=1, x_dtype=0, y_dtype=0, algo=0, y_group=0, in_quant=0, stage1_rows=0,
                 fused_waves=0, fused_block=0, stage2_rows=0, stage2_cols=0,
-                stage2_waves=0)
+                stage2_waves=0, stage3_lanes=0)
     base.update(kw)
     keep = []
 
@@ -57,7 +57,7 @@ def _create(**kw):
                    base["group"], base["N"], base["Cin"], base["Cout"], base["H"], base["W"],
                    base["pad"], base["x_dtype"], base["y_dtype"], base["algo"], base["y_group"],
                    base["in_quant"], base["stage1_rows"], base["fused_waves"], base["fused_block"],
-                   base["stage2_rows"], base["stage2_cols"], base["stage2_waves"])
+                   base["stage2_rows"], base["stage2_cols"], base["stage2_waves"], base["stage3_lanes"])
     h = C.c_void_p()
     st = B.wq8_plan_create(d, h)
     if st == 0:
@@ -97,6 +97,7 @@ def _create(**kw):
     (dict(stage2_rows=1), 0), (dict(stage2_rows=5), 0), (dict(stage2_rows=3), -1), (dict(stage2_rows=7), -1),
     (dict(stage2_cols=2, stage2_rows=5), 0), (dict(stage2_cols=2, stage2_rows=6), -2),
     (dict(stage2_cols=3), -1), (dict(stage2_waves=2), 0), (dict(stage2_waves=3), -1),
+    (dict(stage3_lanes=1), 0), (dict(stage3_lanes=2), 0), (dict(stage3_lanes=3), -1), (dict(stage3_lanes=-1), -1),
 ])
 def test_plan_validation(kw, status):
     assert _create(**kw) == status
