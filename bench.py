@@ -539,8 +539,8 @@ def main():
         traffic_summary(args.layer, *args.traffic_summary, args.copy_mib)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is not "
-              "sharded across GPUs in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library does "
+              "not shard a layer across GPUs", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")

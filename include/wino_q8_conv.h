@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
     WQ8_OK = 0,
     WQ8_ERR_INVALID_ARG = -1,      /* a size, pointer or enum is out of range */
-    WQ8_ERR_UNSUPPORTED = -2,      /* valid, but not a configuration this build runs */
+    WQ8_ERR_UNSUPPORTED = -2,      /* valid, but not a configuration the library runs */
     WQ8_ERR_SINGULAR_POINTS = -3,  /* points not distinct: V is singular */
     WQ8_ERR_WORKSPACE_TOO_SMALL = -4,
     WQ8_ERR_MISALIGNED = -5,       /* a device pointer is not 16-byte aligned */

@@ -330,7 +330,7 @@ static wq8_status build(const wq8_desc *d, wq8_plan *p) {
         n2 * (int64_t)d->Cout * d->Cin >= lim ||
         (int64_t)d->N * d->Cin * d->H * d->W * 4 >= lim ||
         (int64_t)d->N * d->Cout * g.Ho * g.Wo * 4 >= lim)
-        return fail(WQ8_ERR_UNSUPPORTED, "problem too large for this build");
+        return fail(WQ8_ERR_UNSUPPORTED, "problem too large: an array would reach 2^31 bytes (32-bit buffer offsets)");
     p->xdt = d->x_dtype;
     p->ydt = d->y_dtype;
 
