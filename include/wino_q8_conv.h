@@ -37,7 +37,8 @@
  *
  * Conventions for every entry point:
  *   - Device pointers are caller-owned allocations on the current HIP device;
- *     the library never allocates device memory and never synchronises.
+ *     the library never allocates device memory at run time (the workspace of
+ *     wq8_conv_forward_noalloc is a module-scope array) and never synchronises.
  *     All work is enqueued on `stream` (a hipStream_t; NULL = default stream)
  *     and completes asynchronously; device faults surface at the caller's
  *     next synchronisation.
