@@ -20,7 +20,7 @@
  * tH = ceil(Ho/m), tW = ceil(Wo/m), Ho = H + 2 pad - 2, Wo likewise):
  *   U  = G g G^T per (co, ci); codes/scales per group of G input channels
  *        inside one tap:         Uq [n*n][Cout][Cin] int8, sU [n*n][Cout][Cin/G] f32
- *   V  = B^T d B^T^T per (t, ci), d the n x n input patch (zero outside the
+ *   V  = B^T d B per (t, ci), d the n x n input patch (zero outside the
  *        image):                  Vq [n*n][T][Cin] int8,   sV [n*n][T][Cin/G] f32
  *   P_g = sum_{ci in g} Vq Uq (int32, exact)
  *   M  = sum_g (sV_g sU_g) P_g as an fp32 fma chain over g: M [n*n][T][Cout] f32
@@ -77,8 +77,9 @@ typedef enum { WQ8_F32 = 0, WQ8_BF16 = 1 } wq8_dtype;
  *   STAGED: an int8 GEMM kernel writes M (fp32) to the workspace and a second
  *           kernel requantizes it and applies the output transform as fp32
  *           fma chains in index order (bit-identical to that definition);
- *   FUSED:  one kernel keeps M on chip (LDS/registers) per 16 tiles x 16
- *           output channels, re-reading the prepared weights per tile block,
+ *   FUSED:  one kernel keeps M on chip (registers) per block of 16 or 32
+ *           tiles x 16 or 32 output channels, re-reading the prepared
+ *           weights per tile block,
  *           and evaluates vec(O) = (A^T kron A^T) vec(Yq) on fp16 matrix
  *           cores with the Kronecker matrix split into two fp16 parts
  *           (fp32 accumulation): outputs within ~1e-5 of their RMS of the
