@@ -33,6 +33,8 @@ struct Geo {
     int fused_waves;          // fused kernel: waves per 16 x 16 block (4, 8 or 16), 0 chosen at launch
     int fused_wide;           // fused kernel, F(6,3): -1 chosen at launch; 0 16 x 16 blocks; 1 32 x 32,
                               // 2 32 tiles x 16 channels, 3 16 x 32
+    int fused_ntb;            // wide fused kernel: tile blocks (set at launch); block b takes
+                              // tiles [b T / ntb, (b + 1) T / ntb)
     int y_rows;               // 1: one Y scale per row of taps (staged only)
     int in_quant;             // wq8_inq: 0 fp32 input transform, 1/2 integer
     int s1_rows;              // stage-1 window: 0 chosen at launch, 1 all rows, 2 half the rows

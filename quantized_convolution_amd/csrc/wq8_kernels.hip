@@ -19,6 +19,7 @@
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
+#include <utility>
 
 #include "wq8_device.h"
 #include "wq8_internal.h"
@@ -1083,12 +1084,13 @@ __device__ __forceinline__ void fused_build_ktab(const float *at_lds, _Float16 (
 // K[row][tap] * Yq[tap][pair] on fp16 MFMA, for this wave's CBW column blocks
 // cb = wave + WPB c (pairs 16 cb .. 16 cb + 15, code rows in LDS). All of a
 // wave's column blocks cover the same 16 tiles, t0w .. t0w + 15 (lane
-// nl = lane % 16 takes tile t0w + nl); column block c is output channel
+// nl = lane % 16 takes tile t0w + nl; tiles from t_end on belong to no pair
+// of the block and are not stored); column block c is output channel
 // co_base + co_step c. Taps NT..63 of a code row hold stale bytes: finite
 // codes, multiplied by K = 0 there.
 template <int M, int WPB, int CBW, typename YT>
 __device__ __forceinline__ void fused_output(const uint8_t *codes, const _Float16 (*ktab)[M * M * 64],
-                                             const float *s_out, int wave, int t0w, int co_base,
+                                             const float *s_out, int wave, int t0w, int t_end, int co_base,
                                              int co_step, YT *y, const Geo &g) {
     constexpr int BS = M == 6 ? 8 : 4;  // output row a, column b -> product row a * BS + b
     constexpr int RB = M * BS / 16;     // 16-row blocks of the output product
@@ -1119,7 +1121,7 @@ __device__ __forceinline__ void fused_output(const uint8_t *codes, const _Float1
             const int row0 = 16 * rb + 4 * kg;
             const int a = row0 / BS, b0 = row0 % BS;
             const int n = min(4, min(M, wv) - b0);
-            nv[rb] = t < g.T && a < hv && n > 0 ? n : 0;
+            nv[rb] = t < t_end && a < hv && n > 0 ? n : 0;
             ooff[rb] = (base + a * g.Wo + b0) * ES;
         }
     }
@@ -1415,7 +1417,7 @@ __global__ __launch_bounds__(64 * WPB, WPB == 4 && MULTI ? 3 : 4) void k_fused23
 
     // ---- output transform: column block cb = wave + WPB c holds tiles
     // t0 .. t0 + 15 of output channel co0 + cb
-    fused_output<M, WPB, CBW, YT>(codes, ktab, s_out, wave, t0, co0 + wave, WPB, y, g);
+    fused_output<M, WPB, CBW, YT>(codes, ktab, s_out, wave, t0, (int)g.T, co0 + wave, WPB, y, g);
 }
 
 // Wide fused blocks, F(6,3): HT x 16 tiles by HC x 16 output channels, with
@@ -1455,11 +1457,12 @@ __global__ __launch_bounds__(256 * HT * HC, 1) void k_fused23w(const int8_t *__r
     const int lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
     const int nco = (g.Cout + RC - 1) / RC;
-    const int ntb = (int)((g.T + RT - 1) / RT);
+    const int ntb = g.fused_ntb;  // at least ceil(T / RT), so a block has at most RT tiles
     const int blk = xcd_block(blockIdx.x, gridDim.x);
     const int cob = g.co_major ? blk / ntb : blk % nco;
     const int tb = g.co_major ? blk % ntb : blk / nco;
-    const int t0 = tb * RT, co0 = cob * RC;
+    const int t0 = (int)((int64_t)tb * g.T / ntb), t1 = (int)((int64_t)(tb + 1) * g.T / ntb);
+    const int co0 = cob * RC;
     const int tap0 = wave * TPW;
     const size_t vplane = (size_t)g.T * g.Cin, uplane = (size_t)g.Cout * g.Cin;
     float *wlds = reinterpret_cast<float *>(codes) + wave * WLDS;
@@ -1470,7 +1473,8 @@ __global__ __launch_bounds__(256 * HT * HC, 1) void k_fused23w(const int8_t *__r
     fused_build_ktab<M, NTH>(at_lds, ktab, mt.kscale);
 
     // ---- Hadamard GEMMs: A = U rows co0 + 16 hc + r, B = V rows t0 + 16 ht + r
-    // (rows past Cout or T read row 0: they feed pairs that are never stored)
+    // (channel rows past Cout read row 0 and tile rows past the block's last
+    // tile read zero: they feed pairs that are never stored)
     const int n2 = g.n * g.n;
     const auto rV = make_rsrc(Vq, (size_t)n2 * vplane);
     const auto rU = make_rsrc(Uq, (size_t)n2 * uplane);
@@ -1482,7 +1486,7 @@ __global__ __launch_bounds__(256 * HT * HC, 1) void k_fused23w(const int8_t *__r
 #pragma unroll
     for (int h = 0; h < HT; ++h) {
         const int tB = t0 + 16 * h + r;
-        voff[h] = (tB < g.T ? tB : 0) * g.Cin + koff;
+        voff[h] = tB < t1 ? tB * g.Cin + koff : kOob;
     }
 #pragma unroll
     for (int h = 0; h < HC; ++h) {
@@ -1543,7 +1547,7 @@ __global__ __launch_bounds__(256 * HT * HC, 1) void k_fused23w(const int8_t *__r
             const int tap = tap0 + j;
             int off;
             if (isv) {
-                const int tr = t0 + row < g.T ? t0 + row : 0;
+                const int tr = t0 + row < t1 ? t0 + row : 0;
                 off = ((tap * (int)g.T + tr) * g.ng + gi) * 4;
             } else {
                 const int cr = co0 + row < g.Cout ? co0 + row : 0;
@@ -1650,7 +1654,7 @@ __global__ __launch_bounds__(256 * HT * HC, 1) void k_fused23w(const int8_t *__r
     // ---- output transform: column block cb = wave + WPB c holds pairs
     // 16 cb .. 16 cb + 15, i.e. channel co0 + cb / HT and tiles
     // t0 + 16 (cb % HT) + 0..15; cb % HT == wave % HT for all of a wave's blocks
-    fused_output<M, WPB, CBW, YT>(codes, ktab, s_out, wave, t0 + 16 * (wave % HT), co0 + wave / HT, WPB / HT,
+    fused_output<M, WPB, CBW, YT>(codes, ktab, s_out, wave, t0 + 16 * (wave % HT), t1, co0 + wave / HT, WPB / HT,
                                   y, g);
 }
 
@@ -1875,14 +1879,28 @@ static void stage3_m(const Geo &g, const Mats &mt, const float *Mi, YT *y, int8_
 //   56 x 56 ResNet-18 layer. 16 waves were never faster.
 //   Wide blocks (F(6,3), G <= 64) let each tap's operands feed two MFMAs
 //   (48 operand rows per block instead of 2 x 32 for two 16 x 16 blocks).
-//   The busiest CU loads ceil(blocks / CUs) x (tile rows + channel rows)
-//   operand rows per tap and K byte; the shape with the fewest wins, ties to
-//   16 x 32, then 32 x 16. Measured fused stage (16 x 16 -> 16 x 32): 56 x 56
-//   ResNet-18 layer 18.5 -> 15.4 us, 28 x 28 22.8 -> 20.2 us, 14 x 14
-//   39.1 -> 31.6 us; where 16 x 16 blocks already give each CU one block
-//   (7 x 7, C = 512) the model keeps them (42 vs 61 us). 32 x 32 blocks of
-//   16 waves run slower than the model says on those layers and are only
-//   taken when forced.
+//   The busiest CU loads (its blocks) x (tile rows + channel rows) operand
+//   rows per tap and K byte; the shape with the fewest wins, ties to 16 x 32,
+//   then 32 x 16. A wide block holds T / ntb tiles (fused_tile_blocks), a
+//   16 x 16 block 16. Measured fused stage (16 x 16 -> 16 x 32, 16-tile
+//   wide blocks): 56 x 56 ResNet-18 layer 18.5 -> 15.4 us, 28 x 28 22.8 ->
+//   20.2 us, 14 x 14 39.1 -> 31.6 us; where 16 x 16 blocks already give each
+//   CU one block (7 x 7, C = 512) the model keeps them (42 vs 61 us). With
+//   the tile blocks evened out over the CUs the model picks 32 x 16 on the
+//   56 x 56 and 28 x 28 layers (15.4 -> 15.1 us, 20.4 -> 18.6 us). 32 x 32
+//   blocks of 16 waves run slower than the model says on those layers and
+//   are only taken when forced.
+// Tile blocks of the wide fused kernel. At least ceil(T / rt), so that no
+// block holds more than rt tiles; raised so that the blocks come out to the
+// same count on every compute unit. With b blocks on the busiest unit either
+// way, each block then holds T / ntb tiles instead of rt, so that unit loads
+// fewer tile rows (its weight rows are the same).
+static int64_t fused_tile_blocks(int64_t T, int rt, int64_t nco, int cus) {
+    const int64_t ntb0 = (T + rt - 1) / rt;
+    const int64_t per = (ntb0 * nco + cus - 1) / cus;  // blocks of the busiest unit
+    return std::max(ntb0, std::min(T, per * cus / nco));
+}
+
 static void fused_shape(const Geo &g, int cus, int &waves, int &wide) {
     const int64_t nblk = ((g.T + 15) / 16) * (int64_t)((g.Cout + 15) / 16);
     waves = g.fused_waves ? g.fused_waves : g.m == 6 && nblk < 3 * (int64_t)cus ? 8 : 4;
@@ -1892,13 +1910,20 @@ static void fused_shape(const Geo &g, int cus, int &waves, int &wide) {
     }
     wide = 0;
     if (g.m == 6 && g.G <= 64) {
-        auto busiest = [&](int64_t rt, int64_t rc) {
-            const int64_t nb = ((g.T + rt - 1) / rt) * ((g.Cout + rc - 1) / rc);
-            return ((nb + cus - 1) / cus) * (rt + rc);
+        // operand rows of the busiest CU per tap and K byte, in units of 1 / ntb
+        // rows (wide blocks hold T / ntb tiles, 16 x 16 blocks 16)
+        auto busiest = [&](int64_t rt, int64_t rc, bool even) {
+            const int64_t nco = (g.Cout + rc - 1) / rc;
+            const int64_t per = (((g.T + rt - 1) / rt) * nco + cus - 1) / cus;
+            const int64_t ntb = even ? fused_tile_blocks(g.T, (int)rt, nco, cus) : (g.T + rt - 1) / rt;
+            return std::make_pair(per * (even ? g.T : rt * ntb) + per * rc * ntb, ntb);
         };
-        const int64_t c0 = busiest(16, 16), c2 = busiest(32, 16), c3 = busiest(16, 32);
-        if (c3 <= c2 && c3 < c0) wide = 3;
-        else if (c2 < c0) wide = 2;
+        auto less = [](std::pair<int64_t, int64_t> a, std::pair<int64_t, int64_t> b) {
+            return (__int128)a.first * b.second < (__int128)b.first * a.second;
+        };
+        const auto c0 = busiest(16, 16, false), c2 = busiest(32, 16, true), c3 = busiest(16, 32, true);
+        if (!less(c2, c3) && less(c3, c0)) wide = 3;
+        else if (less(c2, c0)) wide = 2;
     }
 }
 
@@ -1906,20 +1931,24 @@ template <int M, int G, typename YT>
 static void fused_m_g(const Geo &g, const Mats &mt, const int8_t *Vq, const float *sV,
                       const int8_t *Uq, const float *sU, YT *y, hipStream_t s) {
     const unsigned blocks = (unsigned)(((g.T + 15) / 16) * ((g.Cout + 15) / 16));
+    const int cus = device_cus();
     int waves, wide;
-    fused_shape(g, device_cus(), waves, wide);
+    fused_shape(g, cus, waves, wide);
     if constexpr (M == 6 && G <= 64) {
         if (wide) {
             // 1: 32 x 32 blocks, 2: 32 tiles x 16 channels, 3: 16 tiles x 32 channels
             const int ht = wide == 3 ? 1 : 2, hc = wide == 2 ? 1 : 2;
-            const unsigned wblocks = (unsigned)(((g.T + 16 * ht - 1) / (16 * ht)) * ((g.Cout + 16 * hc - 1) / (16 * hc)));
+            const int64_t nco = (g.Cout + 16 * hc - 1) / (16 * hc);
+            Geo gw = g;
+            gw.fused_ntb = (int)fused_tile_blocks(g.T, 16 * ht, nco, cus);
+            const unsigned wblocks = (unsigned)(gw.fused_ntb * nco);
             const dim3 th(256 * ht * hc);
 #define WQ8_WIDE(HT_, HC_)                                                                                   \
     do {                                                                                                     \
         if (g.ng == 1)                                                                                       \
-            hipLaunchKernelGGL((k_fused23w<M, G, HT_, HC_, false, YT>), dim3(wblocks), th, 0, s, Vq, sV, Uq, sU, y, mt, g); \
+            hipLaunchKernelGGL((k_fused23w<M, G, HT_, HC_, false, YT>), dim3(wblocks), th, 0, s, Vq, sV, Uq, sU, y, mt, gw); \
         else                                                                                                 \
-            hipLaunchKernelGGL((k_fused23w<M, G, HT_, HC_, true, YT>), dim3(wblocks), th, 0, s, Vq, sV, Uq, sU, y, mt, g);  \
+            hipLaunchKernelGGL((k_fused23w<M, G, HT_, HC_, true, YT>), dim3(wblocks), th, 0, s, Vq, sV, Uq, sU, y, mt, gw);  \
     } while (0)
             if (ht == 2 && hc == 2) WQ8_WIDE(2, 2);
             else if (ht == 2) WQ8_WIDE(2, 1);
