@@ -143,7 +143,10 @@ typedef struct {
     int fused_waves;       /* waves of a 16 x 16 fused block: 4; 8 or 16 for F(6,3) */
     int fused_block;       /* fused block: 1 16 tiles x 16 output channels;
                               F(6,3) with G <= 64 also 2 32 x 32, 3 32 tiles x
-                              16 channels, 4 16 tiles x 32 channels */
+                              16 channels, 4 16 tiles x 32 channels (these
+                              wide blocks hold at most that many tiles: the
+                              launch spreads the tiles evenly over the
+                              compute units) */
     int stage2_rows;       /* staged Hadamard GEMM: 1 the LDS-pipelined kernel
                               (64 tiles x 64 channels per block); 4, 5, 6 or 8
                               the register-streamed kernel with that many
