@@ -1,5 +1,6 @@
 """Host-side checks of bench.py's bookkeeping: the recorded HBM counters are
-tied to the kernel source's code, not to its comments or layout."""
+tied to the kernel source's code, not to its comments or layout; kernel names
+map to stages; a request for more than one GPU is refused."""
 import json
 import os
 
@@ -51,3 +52,13 @@ def test_stage_of_reads_the_template_arguments():
     assert bench.stage_of("void wq8::k_hgemm<32, 5, 1, 4, false>(a)") == "stage2"
     assert bench.stage_of("void wq8::k_stage3<6, false, float>(a)") == "stage3"
     assert bench.stage_of("void wq8::k_weights<6, 64>(a)") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    # the measurement is one GPU's; asking for more exits before any GPU work
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
