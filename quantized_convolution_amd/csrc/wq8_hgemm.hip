@@ -396,6 +396,37 @@ __global__ __launch_bounds__(64 * NWV) void k_hgemm(const int8_t *__restrict__ V
     if constexpr (!I32) {
         float *Mp = Mo + (size_t)ps.tap * g.T * g.Cout;
         const bool vec = g.Cout % 4 == 0;
+        typedef float f4v __attribute__((ext_vector_type(4)));
+        if constexpr (C::CT == 1 && C::BT * (C::BC + 4) * 4 <= (int)sizeof(s_v)) {
+            if (vec) {
+                // M goes through LDS (the V buffers, free after the last
+                // chunk) so that each store instruction writes whole 128-byte
+                // lines of M's rows: a wave's own results cover 64 bytes of a
+                // tile row, and with the non-temporal hint two half-line
+                // stores reach HBM as two writes (31.6 instead of 23.6 MB per
+                // launch on the 1280-channel layer).
+                constexpr int SR = C::BC + 4;  // LDS row stride, floats
+                constexpr int P4 = C::BC / 4;  // 16-byte pieces per row
+                float *sm = reinterpret_cast<float *>(&s_v[0][0]);
+                __syncthreads();  // every wave is done with the V buffers
+#pragma unroll
+                for (int rt = 0; rt < C::RT; ++rt)
+                    *(float4 *)&sm[(16 * rt + r) * SR + 16 * wave + 4 * q] =
+                        float4{acc[0][rt][0], acc[0][rt][1], acc[0][rt][2], acc[0][rt][3]};
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < (C::BT * P4 + C::NT - 1) / C::NT; ++j) {
+                    const int pce = threadIdx.x + C::NT * j;
+                    const int row = pce / P4, c4 = pce % P4;
+                    const int t = ps.t0 + row, co = ps.c0 + 4 * c4;
+                    if (row < C::BT && t < g.T && co < g.Cout) {
+                        const float4 v = *(const float4 *)&sm[row * SR + 4 * c4];
+                        __builtin_nontemporal_store(f4v{v.x, v.y, v.z, v.w}, (f4v *)(Mp + (size_t)t * g.Cout + co));
+                    }
+                }
+                return;
+            }
+        }
         const int wc0 = 16 * C::CT * wave;
 #pragma unroll
         for (int ct = 0; ct < C::CT; ++ct)
@@ -410,7 +441,6 @@ __global__ __launch_bounds__(64 * NWV) void k_hgemm(const int8_t *__restrict__ V
                     // (stage 2 of the 1280-channel layer 47.8 -> 44.2 us; the
                     // same hint on stage 3's 8-byte output stores made that
                     // kernel 1.5-2x slower)
-                    typedef float f4v __attribute__((ext_vector_type(4)));
                     __builtin_nontemporal_store(f4v{acc[ct][rt][0], acc[ct][rt][1], acc[ct][rt][2], acc[ct][rt][3]},
                                                 (f4v *)mp);
                 } else {
