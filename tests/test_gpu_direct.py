@@ -4,8 +4,8 @@ baseline) against the CPU oracle, through the C ABI.
 Bar: activation and weight codes and scales bit-exact; outputs bit-exact as
 well (both sides evaluate the same fp32 fma chain, in the same order, on the
 same codes; no rounding decision follows). Cases span the group sizes,
-padding 0..2, widths that split into several 64-pixel segments with a ragged
-tail, channel counts that are not multiples of 64, bf16 in and out, and the
+padding 0..2, pixel blocks that split a wide row or span several narrow rows
+and images, with a ragged tail, channel counts that are not multiples of 64, bf16 in and out, and the
 full ResNet-18 layer.
 """
 import numpy as np
@@ -38,6 +38,9 @@ CASES = [
     WL.small(WL.LAYERS["c5_f6_n8_c640_32x32_g128"], N=1, H=5, W=6, Cin=256, Cout=9).replace(pad=2, name="g128pad2"),
     WL.small(WL.LAYERS["c5_f6_n8_c1280_16x16_g128"], N=1, H=4, W=3, Cin=256, Cout=3).replace(G=256, name="g256"),
     WL.small(WL.LAYERS["c4_f4_n2_c320_64x64_g64_pert"], N=1, H=3, W=130, Cin=192, Cout=65),
+    # rows narrower than a 64-pixel block: blocks span rows and images, ragged pixel tail
+    WL.small(WL.LAYERS["c5_f6_n8_c1280_16x16_g32"], N=3, H=5, W=7, Cin=96, Cout=40),
+    WL.small(WL.LAYERS["c5_f6_n8_c1280_16x16_g128"], N=2, H=16, W=16, Cin=256, Cout=70),
 ]
 
 
@@ -74,10 +77,12 @@ def test_direct_full_resnet_layer(dev):
     assert np.array_equal(y.cpu().numpy(), ref)
 
 
+# W = 11: blocks of consecutive pixels across rows; W = 40: row blocks
+@pytest.mark.parametrize("W", [11, 40])
 @pytest.mark.parametrize("xdt,ydt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.bfloat16)])
-def test_direct_bf16(dev, xdt, ydt):
-    L = WL.small(WL.LAYERS["c2_f6_n32_c64_56x56_g64"], N=1, H=8, W=11, Cin=64, Cout=24)
-    print(f"\n[case] direct W8A8 bf16 {xdt} -> {ydt}", flush=True)
+def test_direct_bf16(dev, xdt, ydt, W):
+    L = WL.small(WL.LAYERS["c2_f6_n32_c64_56x56_g64"], N=1, H=8, W=W, Cin=64, Cout=24)
+    print(f"\n[case] direct W8A8 bf16 {xdt} -> {ydt} W={W}", flush=True)
     d = WL.make(L)
     xt = torch.from_numpy(d["x"]).to(xdt)
     x_ref = d["x"] if xdt == torch.float32 else oracle.bf16_bits_to_f32(
