@@ -233,7 +233,12 @@ __global__ __launch_bounds__(256) void k_dconv_flat(const int8_t *__restrict__ x
     // position (a tap adds a uniform delta) and the A row
     int xb[2], wb[2];
 #pragma unroll
-    for (int ip = 0; ip < 2; ++ip) xb[ip] = ((pimg[ip] * g.H + pho[ip]) * g.W + pwo[ip]) * g.Cin + koff;
+    for (int ip = 0; ip < 2; ++ip) {
+        // pixels past the layer carry a sentinel row; their offsets are never
+        // used (every tap selects kOob), so row 0 keeps the product in range
+        const int h = pho[ip] < 0 ? 0 : pho[ip];
+        xb[ip] = ((pimg[ip] * g.H + h) * g.W + pwo[ip]) * g.Cin + koff;
+    }
 #pragma unroll
     for (int ic = 0; ic < 2; ++ic) wb[ic] = coA[ic] * g.Cin + koff;
     // operands of step st = (group st / 9, tap st % 9); zero past the last
