@@ -355,12 +355,13 @@ def make_plan(L, d, algo="auto", **kw):
                   s_B=d["s_b"], s_G=d["s_g"], algo=algo, **kw)
 
 
-def run_layer(L, algo, steps, warmup, dev, d=None, cold_reps=20, extras=False):
+def run_layer(L, algo, steps, warmup, dev, d=None, cold_reps=20, extras=False, direct=False):
     """One layer: the forward (K steps captured in one HIP graph and
     replayed between two events; the same K steps eagerly launched for
     comparison), each kernel on its own (its stage entry point captured
     `iters` times), warm and after a cache flush. extras: the literal input
-    stage and the W8A8 direct baseline on the same workload."""
+    stage and the W8A8 direct baseline on the same workload; direct: the
+    W8A8 direct baseline only."""
     d = WL.make(L) if d is None else d
     plan = make_plan(L, d, algo)
     x = torch.from_numpy(d["x"]).to(dev)
@@ -419,6 +420,8 @@ def run_layer(L, algo, steps, warmup, dev, d=None, cold_reps=20, extras=False):
                nbytes=nbytes, tops=L.direct_ops() / (ms * 1e-3) / 1e12,
                cold=(statistics.median(cold), min(cold)))
     if not extras:
+        if direct:
+            out["direct"] = time_direct(L, plan, x, w, y, ms, max(5, iters // 4), dev)
         return out
     # the literal input stage (quantized B^T and input patch, integer
     # transform): its stage-1 kernel and whole forward on the same workload
@@ -438,33 +441,44 @@ def run_layer(L, algo, steps, warmup, dev, d=None, cold_reps=20, extras=False):
                    "forward_us": round(fw * 1e3, 2),
                    "TOPS": round(L.direct_ops() / (fw * 1e-3) / 1e12, 2)}
     out["literal"] = lit
-    # the non-Winograd baseline on the same layer: group-wise W8A8 direct conv
+    out["direct"] = time_direct(L, plan, x, w, y, ms, max(5, iters // 4), dev)
+    return out
+
+
+def time_direct(L, plan, x, w, y, wino_ms, reps, dev):
+    """The non-Winograd baseline on the same layer and inputs: the group-wise
+    W8A8 direct convolution (activation quantization + convolution), each
+    part and the whole forward captured `reps` times in a HIP graph."""
+    stream = torch.cuda.current_stream()
     Wq, sW = q.wq8_direct_weights_prepare(plan, w)
     dws = torch.empty(plan.direct_workspace_bytes, dtype=torch.uint8, device=dev)
     Xq, sX = q.wq8_direct_quantize_x(plan, x)
-    dn = max(5, iters // 4)
     res = {}
     for key, fn in (("forward", lambda: q.wq8_direct_forward(plan, x, Wq, sW, y=y, workspace=dws)),
                     ("quantize_x", lambda: q.wq8_direct_quantize_x(plan, x, Xq, sX)),
                     ("conv", lambda: q.wq8_direct_conv(plan, Xq, sX, Wq, sW, y=y))):
-        gd = capture(fn, dn)
-        res[key] = time_graph(gd, dn, stream)
+        gd = capture(fn, reps)
+        res[key] = time_graph(gd, reps, stream)
         del gd
-    out["direct"] = {"us": round(res["forward"] * 1e3, 2), "quantize_x_us": round(res["quantize_x"] * 1e3, 2),
-                     "conv_us": round(res["conv"] * 1e3, 2),
-                     "TOPS": round(L.direct_ops() / (res["forward"] * 1e-3) / 1e12, 2),
-                     "winograd_speedup": round(res["forward"] / ms, 3)}
-    return out
+    return {"us": round(res["forward"] * 1e3, 2), "quantize_x_us": round(res["quantize_x"] * 1e3, 2),
+            "conv_us": round(res["conv"] * 1e3, 2),
+            "TOPS": round(L.direct_ops() / (res["forward"] * 1e-3) / 1e12, 2),
+            "winograd_speedup": round(res["forward"] / wino_ms, 3)}
 
 
 def layer_entry(L, r):
     """Per-layer record: forward time and throughput, each kernel warm and
-    cold against HBM, and the Hadamard stage against int8 MFMA."""
-    return {"schedule": "fused" if r["plan"].fused else "staged", "tiles": r["plan"].T,
-            "forward_us": round(r["ms"] * 1e3, 2), "TOPS": round(r["tops"], 2),
-            "cold_forward_us": round(r["cold"][0] * 1e3, 2),
-            "cold_TOPS": round(L.direct_ops() / (r["cold"][0] * 1e-3) / 1e12, 2),
-            "eager_forward_us": round(r["eager_ms"] * 1e3, 2), "stages": r["stages"]}
+    cold against HBM, the Hadamard stage against int8 MFMA, and (when timed)
+    the W8A8 direct baseline with the Winograd speedup over it."""
+    e = {"schedule": "fused" if r["plan"].fused else "staged", "tiles": r["plan"].T,
+         "forward_us": round(r["ms"] * 1e3, 2), "TOPS": round(r["tops"], 2),
+         "cold_forward_us": round(r["cold"][0] * 1e3, 2),
+         "cold_TOPS": round(L.direct_ops() / (r["cold"][0] * 1e-3) / 1e12, 2),
+         "eager_forward_us": round(r["eager_ms"] * 1e3, 2), "stages": r["stages"]}
+    if "direct" in r:
+        e["direct_w8a8_us"] = r["direct"]["us"]
+        e["winograd_speedup"] = r["direct"]["winograd_speedup"]
+    return e
 
 
 def stage_calls(plan, x, Uq, sU, y, dev):
@@ -595,7 +609,7 @@ def main():
                 layers[name] = layer_entry(L, r)
                 continue
             layers[name] = layer_entry(Lx, run_layer(Lx, "auto", min(args.steps, 100),
-                                                     min(args.warmup, 10), dev))
+                                                     min(args.warmup, 10), dev, direct=True))
         out["layers"] = layers
     out["accuracy"] = accuracy(L, r["d"], dev, images=min(L.N, 4 if L.N >= 32 else 2))
     if not args.no_cpu_baseline:
