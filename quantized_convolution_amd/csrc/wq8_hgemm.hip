@@ -60,6 +60,11 @@ struct H2 {
     static constexpr int LPV = (BT * PPR + NT - 1) / NT; // V pieces per thread per chunk
     static constexpr int SPV = (BT * GPC + NT - 1) / NT; // V scales per thread per chunk
     static constexpr int SPU = (BC * GPC + NT - 1) / NT; // U scales per thread per chunk
+    // LDS rows the threads' pieces cover (at least BT, BC): the rows past the
+    // block's take the zeros loaded for them, so the commit needs no bounds
+    static constexpr int VR = LPV * NT / PPR;            // V rows
+    static constexpr int SVR = SPV * NT / GPC;           // V scale rows per group
+    static constexpr int SUR = SPU * NT / GPC;           // U scale rows per group
     static constexpr bool K64 = G >= 64;
     static constexpr int NK = K64 ? G / 64 : 1;          // MFMA steps per group
     // U registers per lane per chunk and channel tile, in 16-byte pieces
@@ -149,17 +154,28 @@ __device__ __forceinline__ void h2_issue_v(H2Stage<C> &st, int c, int nch, const
     for (int j = 0; j < C::LPV; ++j) st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rV, (int)(bs.v[j] + cb), 0, 0);
     if constexpr (!I32) {
         const uint32_t sb = c < nch ? (uint32_t)(c * C::GPC * 4) : (uint32_t)kOob;
+        // groups of 32 run every group slot of a chunk: the slots past the
+        // row's last group load zero scales, so fma(0, P, M) leaves M as it
+        // is (M is never -0: its chain starts at +0 and no scale is negative)
+        const int gend = g.ng - c * C::GPC;
 #pragma unroll
-        for (int j = 0; j < C::SPV; ++j)
-            st.sv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsV, (int)(bs.sv[j] + sb), 0, 0));
+        for (int j = 0; j < C::SPV; ++j) {
+            const int k = (threadIdx.x + C::NT * j) % C::GPC;
+            const uint32_t o = C::G != 32 || k < gend ? bs.sv[j] + sb : (uint32_t)kOob;
+            st.sv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsV, (int)o, 0, 0));
+        }
 #pragma unroll
-        for (int j = 0; j < C::SPU; ++j)
-            st.su[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsU, (int)(bs.su[j] + sb), 0, 0));
+        for (int j = 0; j < C::SPU; ++j) {
+            const int k = (threadIdx.x + C::NT * j) % C::GPC;
+            const uint32_t o = C::G != 32 || k < gend ? bs.su[j] + sb : (uint32_t)kOob;
+            st.su[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsU, (int)o, 0, 0));
+        }
     }
 }
 
-// Write a chunk of V (rows 0..BT-1) and its scales, transposed to
-// [group][row], to LDS.
+// Write a chunk of V (rows 0..VR-1; rows from BT on hold zeros) and its
+// scales, transposed to [group][row], to LDS. No bounds: every thread's
+// pieces have rows in the padded buffers.
 template <class C, bool I32>
 __device__ __forceinline__ void h2_commit_v(const H2Stage<C> &st, int8_t *op, float *ssv, float *ssu) {
     const int tid = threadIdx.x;
@@ -167,15 +183,13 @@ __device__ __forceinline__ void h2_commit_v(const H2Stage<C> &st, int8_t *op, fl
     for (int j = 0; j < C::LPV; ++j) {
         const int pce = tid + C::NT * j;
         const int row = pce / C::PPR, qq = pce % C::PPR;
-        if (row < C::BT) {
-            int8_t *p = &op[row * C::LDR + 16 * qq];
-            if constexpr (C::LDR % 16 == 0) {
-                *(v4i *)p = st.v[j];
-            } else {  // rows are 8-byte aligned
-                typedef int v2i __attribute__((ext_vector_type(2)));
-                ((v2i *)p)[0] = v2i{st.v[j].x, st.v[j].y};
-                ((v2i *)p)[1] = v2i{st.v[j].z, st.v[j].w};
-            }
+        int8_t *p = &op[row * C::LDR + 16 * qq];
+        if constexpr (C::LDR % 16 == 0) {
+            *(v4i *)p = st.v[j];
+        } else {  // rows are 8-byte aligned
+            typedef int v2i __attribute__((ext_vector_type(2)));
+            ((v2i *)p)[0] = v2i{st.v[j].x, st.v[j].y};
+            ((v2i *)p)[1] = v2i{st.v[j].z, st.v[j].w};
         }
     }
     if constexpr (!I32) {
@@ -183,13 +197,13 @@ __device__ __forceinline__ void h2_commit_v(const H2Stage<C> &st, int8_t *op, fl
         for (int j = 0; j < C::SPV; ++j) {
             const int e = tid + C::NT * j;
             const int row = e / C::GPC, k = e % C::GPC;
-            if (row < C::BT) ssv[k * C::BT + row] = st.sv[j];
+            ssv[k * C::SVR + row] = st.sv[j];
         }
 #pragma unroll
         for (int j = 0; j < C::SPU; ++j) {
             const int e = tid + C::NT * j;
             const int row = e / C::GPC, k = e % C::GPC;
-            if (row < C::BC) ssu[k * C::BC + row] = st.su[j];
+            ssu[k * C::SUR + row] = st.su[j];
         }
     }
 }
@@ -248,7 +262,14 @@ __device__ __forceinline__ void h2_chunk(float (&acc)[C::CT][C::RT][4], v4i (&u)
     }
 #pragma unroll
     for (int k = 0; k < C::GPC; ++k) {
-        if (k >= gin) break;
+        // groups of 32 (M only) run every group slot of the chunk: slots past
+        // the row's last group have zero scales (h2_issue_v) and leave M as
+        // it is; the fence keeps the groups in order, as the branch did
+        if constexpr (I32 || C::G != 32) {
+            if (k >= gin) break;
+        } else {
+            __builtin_amdgcn_sched_barrier(0);
+        }
         v4i P[C::CT][C::RT];
 #pragma unroll
         for (int ct = 0; ct < C::CT; ++ct)
@@ -310,9 +331,9 @@ __device__ __forceinline__ void h2_chunk(float (&acc)[C::CT][C::RT][4], v4i (&u)
             float4 su[C::CT];
             float sv[C::RT];
 #pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) su[ct] = *(const float4 *)&ssu[k * C::BC + wc0 + 16 * ct + 4 * q];
+            for (int ct = 0; ct < C::CT; ++ct) su[ct] = *(const float4 *)&ssu[k * C::SUR + wc0 + 16 * ct + 4 * q];
 #pragma unroll
-            for (int rt = 0; rt < C::RT; ++rt) sv[rt] = ssv[k * C::BT + 16 * rt + r];
+            for (int rt = 0; rt < C::RT; ++rt) sv[rt] = ssv[k * C::SVR + 16 * rt + r];
 #pragma unroll
             for (int ct = 0; ct < C::CT; ++ct) {
                 const float sus[4] = {su[ct].x, su[ct].y, su[ct].z, su[ct].w};
@@ -334,9 +355,9 @@ __global__ __launch_bounds__(64 * NWV) void k_hgemm(const int8_t *__restrict__ V
                                                     float *__restrict__ Mo, int32_t *__restrict__ Po,
                                                     Geo g) {
     using C = H2<G, RT, CT, NWV>;
-    __shared__ __attribute__((aligned(16))) int8_t s_v[2][C::BT * C::LDR];
-    __shared__ __attribute__((aligned(16))) float s_sv[2][C::GPC * C::BT];
-    __shared__ __attribute__((aligned(16))) float s_su[2][C::GPC * C::BC];
+    __shared__ __attribute__((aligned(16))) int8_t s_v[2][C::VR * C::LDR];
+    __shared__ __attribute__((aligned(16))) float s_sv[2][C::GPC * C::SVR];
+    __shared__ __attribute__((aligned(16))) float s_su[2][C::GPC * C::SUR];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, q = lane >> 4;
