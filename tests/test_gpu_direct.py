@@ -41,6 +41,9 @@ CASES = [
     # rows narrower than a 64-pixel block: blocks span rows and images, ragged pixel tail
     WL.small(WL.LAYERS["c5_f6_n8_c1280_16x16_g32"], N=3, H=5, W=7, Cin=96, Cout=40),
     WL.small(WL.LAYERS["c5_f6_n8_c1280_16x16_g128"], N=2, H=16, W=16, Cin=256, Cout=70),
+    # either side of the switch between the two block forms (rows of 32 and 33 pixels)
+    WL.small(WL.LAYERS["c5_f6_n8_c640_32x32_g32"], N=2, H=5, W=32, Cin=64, Cout=36),
+    WL.small(WL.LAYERS["c5_f6_n8_c640_32x32_g32"], N=2, H=5, W=33, Cin=64, Cout=36),
 ]
 
 
