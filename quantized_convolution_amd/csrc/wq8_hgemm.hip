@@ -72,10 +72,11 @@ struct H2 {
     static constexpr int UP = G == 16 ? KC / 32 : KC / 64;
     // U chunks in flight per wave: 4 for the shapes that still fit in 128
     // registers with them (four waves per SIMD; the deeper ring hides more of
-    // HBM's latency when the weights are not cached: 5 % on the 1280-channel
-    // layer), else 2 (more registers would cost a wave per SIMD, which costs
-    // more than the ring gains)
-    static constexpr int DU = RT <= 5 && CT == 1 && NWV == 4 && G >= 32 && G <= 128 ? 4 : 2;
+    // HBM's latency when the weights are not cached), else 2 (more registers
+    // would cost a wave per SIMD, which costs more than the ring gains).
+    // Groups of 32 keep 2: their software-pipelined chunk needs the
+    // registers, and gains more than the deeper ring
+    static constexpr int DU = RT <= 5 && CT == 1 && NWV == 4 && G >= 64 && G <= 128 ? 4 : 2;
 };
 
 struct H2Pos {
@@ -154,9 +155,10 @@ __device__ __forceinline__ void h2_issue_v(H2Stage<C> &st, int c, int nch, const
     for (int j = 0; j < C::LPV; ++j) st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rV, (int)(bs.v[j] + cb), 0, 0);
     if constexpr (!I32) {
         const uint32_t sb = c < nch ? (uint32_t)(c * C::GPC * 4) : (uint32_t)kOob;
-        // groups of 32 run every group slot of a chunk: the slots past the
-        // row's last group load zero scales, so fma(0, P, M) leaves M as it
-        // is (M is never -0: its chain starts at +0 and no scale is negative)
+        // groups of 32 (M only, h2_chunk_pipe32) run every group slot of a
+        // chunk: the slots past the row's last group load zero scales, so
+        // fma(0, P, M) leaves M as it is (M is never -0: its chain starts at
+        // +0 and no scale is negative)
         const int gend = g.ng - c * C::GPC;
 #pragma unroll
         for (int j = 0; j < C::SPV; ++j) {
@@ -236,6 +238,77 @@ __device__ __forceinline__ long pack64(int lo, int hi) {
     return (long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
+// Groups of 32, M only: B fragment (8 bytes of tile row 16 rt + r; K-slot q
+// carries bytes 16 (q & 1) + 8 (q >> 1) of group k) and A fragment (8 bytes
+// of channel tile ct's group k; each 16-byte piece of U holds 8 bytes of two
+// groups after the swap).
+template <class C>
+__device__ __forceinline__ long h2_bfrag32(const int8_t *sb, int k, int rt, int r, int q) {
+    return *(const long *)&sb[(16 * rt + r) * C::LDR + 32 * k + 16 * (q & 1) + 8 * (q >> 1)];
+}
+
+template <class C>
+__device__ __forceinline__ long h2_afrag32(const v4i (&u)[C::CT][C::UP], int k, int ct) {
+    const v4i w = u[ct][k >> 1];
+    return (k & 1) ? pack64(w.z, w.w) : pack64(w.x, w.y);
+}
+
+// A chunk for groups of 32 (M only), software-pipelined over its GPC group
+// slots: right after the dequantization of group k has read a 16x16 block's
+// products, the block's MFMA of group k + 1 writes the same registers, so a
+// wave's matrix core works on the next group while its vector ALU
+// dequantizes the current one; the next group's B fragments are read from
+// LDS before that dequantization starts. Every output's fma chain still runs
+// over the groups in ascending order (M is bit-identical to one group at a
+// time). Slots past a row's last group have zero scales (h2_issue_v), so
+// fma(0, P, M) leaves M as it is. The scheduling fences keep the compiler
+// from hoisting later groups' reads, which would cost registers and a wave
+// per SIMD.
+template <class C>
+__device__ __forceinline__ void h2_chunk_pipe32(float (&acc)[C::CT][C::RT][4], const v4i (&u)[C::CT][C::UP],
+                                                const int8_t *sb, const float *ssv, const float *ssu) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, q = lane >> 4;
+    const int wc0 = 16 * C::CT * wave;
+    const v4i zero = v4i{0, 0, 0, 0};
+    v4i P[C::CT][C::RT];
+    long bb[C::RT];
+#pragma unroll
+    for (int rt = 0; rt < C::RT; ++rt) bb[rt] = h2_bfrag32<C>(sb, 0, rt, r, q);
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+        for (int rt = 0; rt < C::RT; ++rt)
+            P[ct][rt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(h2_afrag32<C>(u, 0, ct), bb[rt], zero, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < C::GPC; ++k) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + 1 < C::GPC) {
+#pragma unroll
+            for (int rt = 0; rt < C::RT; ++rt) bb[rt] = h2_bfrag32<C>(sb, k + 1, rt, r, q);
+        }
+        float4 su[C::CT];
+        float sv[C::RT];
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) su[ct] = *(const float4 *)&ssu[k * C::SUR + wc0 + 16 * ct + 4 * q];
+#pragma unroll
+        for (int rt = 0; rt < C::RT; ++rt) sv[rt] = ssv[k * C::SVR + 16 * rt + r];
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) {
+            const float sus[4] = {su[ct].x, su[ct].y, su[ct].z, su[ct].w};
+            const long a = k + 1 < C::GPC ? h2_afrag32<C>(u, k + 1, ct) : 0;
+#pragma unroll
+            for (int rt = 0; rt < C::RT; ++rt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[ct][rt][i] = __builtin_fmaf(sv[rt] * sus[i], (float)P[ct][rt][i], acc[ct][rt][i]);
+                if (k + 1 < C::GPC) P[ct][rt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bb[rt], zero, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+}
+
 // One chunk: GPC groups (gin of them present), A from the U ring slot, B
 // from the V buffer in LDS.
 template <class C, bool I32>
@@ -260,16 +333,13 @@ __device__ __forceinline__ void h2_chunk(float (&acc)[C::CT][C::RT][4], v4i (&u)
                 u[ct][p] = v4i{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
             }
     }
+    if constexpr (!I32 && C::G == 32) {
+        h2_chunk_pipe32<C>(acc, u, sb, ssv, ssu);
+        return;
+    }
 #pragma unroll
     for (int k = 0; k < C::GPC; ++k) {
-        // groups of 32 (M only) run every group slot of the chunk: slots past
-        // the row's last group have zero scales (h2_issue_v) and leave M as
-        // it is; the fence keeps the groups in order, as the branch did
-        if constexpr (I32 || C::G != 32) {
-            if (k >= gin) break;
-        } else {
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        if (k >= gin) break;
         v4i P[C::CT][C::RT];
 #pragma unroll
         for (int ct = 0; ct < C::CT; ++ct)
